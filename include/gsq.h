@@ -1,0 +1,232 @@
+/*
+ * gsq.h -- C ABI of the GSQ relaxed-quantization step on AMD MI355X (gfx950).
+ *
+ * The method (paper "GSQ: Highly-Accurate Low-Precision Scalar Quantization for
+ * LLMs via Gumbel-Softmax Sampling"): every weight coordinate of a linear layer
+ * W [rows x cols] carries learnable logits over a symmetric scalar grid with one
+ * scale per group of 128 consecutive in-features; a Gumbel-Softmax sample of
+ * the logits at temperature tau gives a soft weight; the layer's output
+ * reconstruction error on calibration activations is minimised over the logits
+ * and the group scales with Lion while tau is annealed; the logits are then
+ * collapsed to hard codes that existing scalar kernels consume
+ * (agihunt.info summary: idea, method and optimizer paragraphs; atlas.scime.ai
+ * summary: Approach; thelatestinai.com abstract).
+ *
+ * One optimisation step is four calls, in this order, on one stream:
+ *   gsq_relax_fwd        soft weights -> dW = W_soft - W (bf16)
+ *   gsq_recon_loss_grad  R = X dW^T, loss = sum R^2, G = 2 R^T X
+ *   gsq_relax_bwd_lion   dLoss/dlogits, dLoss/dscales, Lion on both, in place
+ * and, once after the last step,
+ *   gsq_harden_pack      argmax codes, packed bit-stream, fp16 scales.
+ *
+ * Conventions for every call:
+ *  - Pointers named as tensors are DEVICE pointers, allocated and owned by the
+ *    caller; the library allocates and frees no memory and keeps no mutable
+ *    global state. Host pointers are marked "host".
+ *  - Device tensors must be 16-byte aligned (GSQ_ERR_ALIGN otherwise).
+ *  - Layouts are row-major. Logits and their Lion momentum are planar
+ *    [L][rows][cols] fp32 (plane k holds logit k of every coordinate), with
+ *    L = 4 (2-bit), 2 (ternary: plane 0 mask, plane 1 sign), 5 (3-bit local
+ *    shift: planes for offsets -2..+2). Scales and their momentum are
+ *    [rows][cols/128] fp32. bf16 and fp16 tensors are passed as uint16_t bits.
+ *  - All arguments are checked before anything is launched; a failed check
+ *    returns its status and launches nothing. A HIP launch error returns
+ *    GSQ_ERR_HIP. Work is asynchronous and ordered on `stream` (a hipStream_t,
+ *    NULL for the default stream). Calls on distinct streams are thread-safe
+ *    when their output tensors do not overlap.
+ *  - Noise is counter-based Philox4x32-10 (Salmon et al., SC'11), so the
+ *    forward and backward of one step regenerate identical noise and a step is
+ *    a pure function of (seed, stream id, step, inputs). Coordinate
+ *    i = row*cols + col uses stream elements e = i*L + k (k = 0..L-1); element
+ *    e is word (e & 3) of the block with counter (lo32(e>>2), hi32(e>>2),
+ *    step, stream id) and key (lo32(seed), hi32(seed)); its uniform is
+ *    ((word >> 8) | 1) * 2^-24.
+ */
+#ifndef GSQ_H_
+#define GSQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GSQ_ABI_VERSION 1
+
+typedef enum {
+    GSQ_OK = 0,
+    GSQ_ERR_NULL = 1,   /* a required pointer is NULL */
+    GSQ_ERR_SHAPE = 2,  /* a size is out of range or not a required multiple */
+    GSQ_ERR_ALIGN = 3,  /* a device tensor is not 16-byte aligned */
+    GSQ_ERR_GRID = 4,   /* unknown grid, or a grid-specific argument missing */
+    GSQ_ERR_PARAM = 5,  /* a scalar is out of range (tau, noise scale, Lion) */
+    GSQ_ERR_HIP = 6     /* the HIP runtime reported an error at launch */
+} gsq_status;
+
+/* Grids (agihunt.info summary, method paragraph). Values in scale units:
+ *  INT2        4 levels {-3,-1,1,3}, 4 logits per coordinate;
+ *  TERNARY     {-1,0,1} as a binary mask times a binary sign, 2 logits;
+ *  INT3_LOCAL  8 levels {-7,-5,...,7}; 5 logits for the codes
+ *              clamp(c0 + d, 0, 7), d = -2..2, around a warm-start code c0. */
+typedef enum { GSQ_GRID_INT2 = 0, GSQ_GRID_TERNARY = 1, GSQ_GRID_INT3_LOCAL = 2 } gsq_grid;
+
+typedef enum { GSQ_DTYPE_F32 = 0, GSQ_DTYPE_BF16 = 1 } gsq_dtype;
+
+/* One layer being quantised. */
+typedef struct {
+    int32_t grid;      /* gsq_grid */
+    int32_t group;     /* scale group size along cols; must be 128 */
+    int64_t rows;      /* out features M (> 0) */
+    int64_t cols;      /* in features K (> 0, multiple of 128) */
+    int32_t w_dtype;   /* gsq_dtype of W */
+    uint32_t stream;   /* noise stream id (e.g. a layer index) */
+    uint64_t seed;     /* noise key */
+} gsq_layer;
+
+/* Lion hyper-parameters (Chen et al. 2023; the pages pick Lion for the logits:
+ * agihunt.info optimizer paragraph). For each parameter theta with gradient g
+ * and momentum m: c = beta1*m + (1-beta1)*g; theta -= lr*(sign(c) + wd*theta);
+ * m = beta2*m + (1-beta2)*g. Logits use lr_logit, scales lr_scale. */
+typedef struct {
+    float lr_logit;
+    float lr_scale;
+    float beta1;        /* in [0, 1) */
+    float beta2;        /* in [0, 1) */
+    float weight_decay; /* >= 0 */
+} gsq_lion;
+
+/* ABI version of the loaded library (GSQ_ABI_VERSION). */
+int gsq_abi_version(void);
+
+/* Static, NUL-terminated name of a status code. */
+const char* gsq_status_str(int status);
+
+/* Number of logits per coordinate of a grid (4, 2, 5), or 0 if unknown. */
+int gsq_num_logits(int grid);
+
+/* Warm start by round-to-nearest (the pages start from GPTQ or a GGUF
+ * K-Quant, agihunt.info optimizer paragraph; the solve itself only needs codes
+ * and scales). Per group: s = maxabs / q_max (q_max = 3, 1, 7), a correctly
+ * rounded fp32 division; x = w / s (0 if s = 0); codes: 2-bit and 3-bit
+ * c0 = clamp(rint((x + q_max) * 0.5), 0, 2^b - 1), ternary t0 + 1 with
+ * t0 = clamp(rint(x), -1, 1) (rint: ties to even). Logits: init_logit on the
+ * warm-start level and 0 elsewhere (local shift: plane 2, offset 0); ternary
+ * mask = +init_logit if t0 != 0 else -init_logit, sign = +init_logit if w >= 0
+ * else -init_logit.
+ *   W       [rows][cols] in layer->w_dtype
+ *   scales  out [rows][cols/128] fp32
+ *   codes   out [rows][cols] uint8 (warm-start codes; INT3_LOCAL needs them
+ *           at every later call)
+ *   logits  out [L][rows][cols] fp32
+ * Momenta are not touched: the caller zeroes them. */
+gsq_status gsq_init_rtn(const gsq_layer* layer, const void* W, float* scales,
+                        uint8_t* codes, float* logits, float init_logit,
+                        void* stream);
+
+/* Relaxed forward (agihunt.info method paragraph: soft weighted sum of grid
+ * points). With noise n_k drawn for `step` and eta = noise_scale:
+ *   2-bit / local shift: p = softmax((l + eta*g)/tau), g standard Gumbel,
+ *                        w_hat = sum_k p_k v_k;
+ *   ternary: a = sigmoid((l_m + eta*n_m)/tau), b = sigmoid((l_s + eta*n_s)/tau),
+ *            n standard logistic, w_hat = a * (2b - 1);
+ *   w_soft = s * w_hat;  dW = w_soft - W, rounded to bf16 (nearest even).
+ *   logits      [L][rows][cols] fp32
+ *   scales      [rows][cols/128] fp32
+ *   init_codes  [rows][cols] uint8, required for INT3_LOCAL, else ignored
+ *   W           [rows][cols] in layer->w_dtype
+ *   dW_bf16     out [rows][cols] bf16
+ *   w_soft_dbg  optional out [rows][cols] fp32 (NULL to skip)
+ * tau must be finite and > 0; noise_scale in [0, 1]. */
+gsq_status gsq_relax_fwd(const gsq_layer* layer, const float* logits,
+                         const float* scales, const uint8_t* init_codes,
+                         const void* W, uint32_t step, float tau,
+                         float noise_scale, uint16_t* dW_bf16,
+                         float* w_soft_dbg, void* stream);
+
+/* Workspace bytes gsq_recon_loss_grad needs (loss partials), for E experts
+ * whose token blocks are given by tok_offsets (host, E+1 entries). */
+size_t gsq_recon_workspace_bytes(int32_t n_experts, const int64_t* tok_offsets,
+                                 int64_t rows_per_expert, int64_t cols);
+
+/* Output reconstruction objective on calibration activations (agihunt.info
+ * method paragraph) and its gradient, for one layer (n_experts = 1) or for a
+ * batch of experts that each see their own routed tokens:
+ *   R_e = X_e dW_e^T,  loss = sum_e sum R_e^2 = sum_e ||X_e W_soft_e^T - X_e W_e^T||^2,
+ *   G_e = dLoss/d(dW_e) = 2 R_e^T X_e.
+ * bf16 operands, fp32 accumulation on the matrix cores.
+ *   tok_offsets   host [E+1], tok_offsets[0] = 0, non-decreasing, every entry a
+ *                 multiple of 64 (pad token blocks with zero rows: a zero token
+ *                 adds nothing to loss or gradient)
+ *   rows_per_expert  rows of dW owned by each expert (the layer's rows if E = 1)
+ *   cols          in features (multiple of 128)
+ *   X             [T][cols] bf16, T = tok_offsets[E]
+ *   XT            [cols][T] bf16 laid out per expert: block e is X_e^T
+ *                 [cols][n_e] row-major at element offset cols*tok_offsets[e]
+ *                 (gsq_transpose_tokens builds it)
+ *   dW_bf16       [E*rows_per_expert][cols] bf16
+ *   workspace     device scratch of at least gsq_recon_workspace_bytes()
+ *   RT            out, block e is R_e^T [rows_per_expert][n_e] bf16 at element
+ *                 offset rows_per_expert*tok_offsets[e]
+ *   G             out [E*rows_per_expert][cols] fp32
+ *   loss          out device scalar, fp64 (deterministic fixed-order sum) */
+gsq_status gsq_recon_loss_grad(int32_t n_experts, const int64_t* tok_offsets,
+                               int64_t rows_per_expert, int64_t cols,
+                               const uint16_t* X, const uint16_t* XT,
+                               const uint16_t* dW_bf16, void* workspace,
+                               size_t workspace_bytes, uint16_t* RT, float* G,
+                               double* loss, void* stream);
+
+/* Per-expert transpose of the calibration tokens: XT block e = X_e^T (see
+ * gsq_recon_loss_grad for the layout). Done once per layer. */
+gsq_status gsq_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets,
+                                int64_t cols, const uint16_t* X, uint16_t* XT,
+                                void* stream);
+
+/* Relaxed backward and Lion, in place (agihunt.info method and optimizer
+ * paragraphs). Regenerates the step's noise (same `step`, `tau` and
+ * `noise_scale` as the forward) and, with G = dLoss/dW_soft:
+ *   2-bit / local shift: dL/dl_k = G * s * p_k * (v_k - w_hat) / tau;
+ *   ternary: dL/dl_m = G * s * a(1-a)(2b-1) / tau, dL/dl_s = G * s * 2a b(1-b) / tau;
+ *   dL/ds_g = sum over the 128 coordinates of the group of G * w_hat;
+ * then one Lion update of every logit and every scale with its momentum,
+ * taking sign(c) of c = fma(beta1, m, fp32((1-beta1)*g)).
+ *   G                [rows][cols] fp32
+ *   logits, mom      in/out [L][rows][cols] fp32
+ *   scales, scale_mom in/out [rows][cols/128] fp32
+ *   init_codes       [rows][cols] uint8 for INT3_LOCAL, else ignored
+ *   grad_logits_dbg  optional out [L][rows][cols] fp32, gradient before Lion
+ *   grad_scales_dbg  optional out [rows][cols/128] fp32; give both debug
+ *                    outputs or neither (GSQ_ERR_NULL otherwise) */
+gsq_status gsq_relax_bwd_lion(const gsq_layer* layer, const float* G,
+                              float* logits, float* mom, float* scales,
+                              float* scale_mom, const uint8_t* init_codes,
+                              uint32_t step, float tau, float noise_scale,
+                              const gsq_lion* lion, float* grad_logits_dbg,
+                              float* grad_scales_dbg, void* stream);
+
+/* Collapse to hard codes after annealing (agihunt.info method paragraph) in
+ * the symmetric group-128 format with 16-bit scales (takeaway paragraph;
+ * the 2.13 / 3.13 / 1.71 bits per parameter of the results table).
+ *   codes: 2-bit argmax_k l_k (first index on ties); local shift
+ *   clamp(c0 + argmax - 2, 0, 7); ternary t + 1, t = [l_m >= 0]*(l_s >= 0 ? 1 : -1).
+ *   codes       optional out [rows][cols] uint8
+ *   packed      optional out [rows][cols*b/32] uint32, b = 2, 2, 3 bits; per
+ *               row a little-endian LSB-first bit-stream, code j in bits
+ *               [b*j, b*j + b)
+ *   scales_f16  optional out [rows][cols/128] fp16 bits (nearest even) */
+gsq_status gsq_harden_pack(const gsq_layer* layer, const float* logits,
+                           const float* scales, const uint8_t* init_codes,
+                           uint8_t* codes, uint32_t* packed,
+                           uint16_t* scales_f16, void* stream);
+
+/* Raw Philox words of the noise stream of `step`: out[j] = element first + j
+ * (layout above). For checking the generator. */
+gsq_status gsq_noise_dump(const gsq_layer* layer, uint32_t step, int64_t first,
+                          int64_t count, uint32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSQ_H_ */

@@ -1,0 +1,221 @@
+"""GSQ relaxed-quantization step on AMD MI355X (gfx950).
+
+Python binding of ``libgsq.so`` (C ABI in ``include/gsq.h``). Every function
+here has the name of the C entry point it calls and only marshals arguments:
+torch tensors become device pointers, the current torch stream becomes the
+HIP stream, and a non-OK status raises :class:`GsqError`. All work runs in the
+library's HIP kernels; there is no fallback path. If ``libgsq.so`` has not been
+built, the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "GRID_INT2", "GRID_TERNARY", "GRID_INT3_LOCAL", "DTYPE_F32", "DTYPE_BF16",
+    "GsqError", "GsqLayer", "GsqLion", "lib", "exported_symbols",
+    "gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
+    "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
+    "gsq_transpose_tokens", "gsq_relax_bwd_lion", "gsq_harden_pack", "gsq_noise_dump",
+]
+
+GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL = 0, 1, 2
+DTYPE_F32, DTYPE_BF16 = 0, 1
+N_LOGITS = {GRID_INT2: 4, GRID_TERNARY: 2, GRID_INT3_LOCAL: 5}
+CODE_BITS = {GRID_INT2: 2, GRID_TERNARY: 2, GRID_INT3_LOCAL: 3}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsq.so")
+
+#: Entry points declared in include/gsq.h.
+EXPORTS = ("gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
+           "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
+           "gsq_transpose_tokens", "gsq_relax_bwd_lion", "gsq_harden_pack",
+           "gsq_noise_dump")
+
+
+class GsqError(RuntimeError):
+    def __init__(self, fn: str, status: int, name: str):
+        super().__init__(f"{fn} failed: {name} ({status})")
+        self.status = status
+        self.name = name
+
+
+class GsqLayer(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("w_dtype", ctypes.c_int32), ("stream", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64)]
+
+    @classmethod
+    def make(cls, grid: int, rows: int, cols: int, w_dtype: int = DTYPE_BF16,
+             seed: int = 0, stream: int = 0, group: int = 128) -> "GsqLayer":
+        return cls(grid, group, rows, cols, w_dtype, stream & 0xFFFFFFFF,
+                   seed & 0xFFFFFFFFFFFFFFFF)
+
+
+class GsqLion(ctypes.Structure):
+    _fields_ = [("lr_logit", ctypes.c_float), ("lr_scale", ctypes.c_float),
+                ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("weight_decay", ctypes.c_float)]
+
+    @classmethod
+    def make(cls, lr_logit: float = 1e-3, lr_scale: float = 1e-5, beta1: float = 0.9,
+             beta2: float = 0.99, weight_decay: float = 0.0) -> "GsqLion":
+        return cls(lr_logit, lr_scale, beta1, beta2, weight_decay)
+
+
+_lib = None
+_P = ctypes.c_void_p
+_L = ctypes.POINTER(GsqLayer)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m post_weight_quantization_philox_amd.build` (hipcc, gfx950)")
+    l = ctypes.CDLL(LIB_PATH)
+    st = ctypes.c_int
+    sig = {
+        "gsq_abi_version": (ctypes.c_int, []),
+        "gsq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "gsq_num_logits": (ctypes.c_int, [ctypes.c_int]),
+        "gsq_init_rtn": (st, [_L, _P, _P, _P, _P, ctypes.c_float, _P]),
+        "gsq_relax_fwd": (st, [_L, _P, _P, _P, _P, ctypes.c_uint32, ctypes.c_float,
+                               ctypes.c_float, _P, _P, _P]),
+        "gsq_recon_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, _P, ctypes.c_int64,
+                                                        ctypes.c_int64]),
+        "gsq_recon_loss_grad": (st, [ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                     _P, _P, ctypes.c_size_t, _P, _P, _P, _P]),
+        "gsq_transpose_tokens": (st, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
+        "gsq_relax_bwd_lion": (st, [_L, _P, _P, _P, _P, _P, _P, ctypes.c_uint32, ctypes.c_float,
+                                    ctypes.c_float, ctypes.POINTER(GsqLion), _P, _P, _P]),
+        "gsq_harden_pack": (st, [_L, _P, _P, _P, _P, _P, _P, _P]),
+        "gsq_noise_dump": (st, [_L, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64, _P, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(l, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = l
+    return l
+
+
+def exported_symbols():
+    """Names from EXPORTS that the loaded library defines."""
+    l = lib()
+    return [n for n in EXPORTS if hasattr(l, n)]
+
+
+# ----------------------------------------------------------------------------
+# Marshalling
+# ----------------------------------------------------------------------------
+
+def _ptr(x):
+    """Device pointer of a tensor (or an int address, or None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    if torch.cuda.is_available() and torch.cuda.is_initialized():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise GsqError(fn, status, lib().gsq_status_str(status).decode())
+
+
+def _offsets(tok_offsets):
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(tok_offsets, dtype=np.int64))
+    return arr, arr.ctypes.data
+
+
+# ----------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ----------------------------------------------------------------------------
+
+def gsq_abi_version() -> int:
+    return lib().gsq_abi_version()
+
+
+def gsq_status_str(status: int) -> str:
+    return lib().gsq_status_str(status).decode()
+
+
+def gsq_num_logits(grid: int) -> int:
+    return lib().gsq_num_logits(grid)
+
+
+def gsq_init_rtn(layer: GsqLayer, W, scales, codes, logits, init_logit: float = 2.0,
+                 stream=None):
+    _check("gsq_init_rtn", lib().gsq_init_rtn(ctypes.byref(layer), _ptr(W), _ptr(scales),
+                                              _ptr(codes), _ptr(logits), init_logit,
+                                              _stream(stream)))
+
+
+def gsq_relax_fwd(layer: GsqLayer, logits, scales, init_codes, W, step: int, tau: float,
+                  noise_scale: float, dW_bf16, w_soft_dbg=None, stream=None):
+    _check("gsq_relax_fwd", lib().gsq_relax_fwd(ctypes.byref(layer), _ptr(logits), _ptr(scales),
+                                                _ptr(init_codes), _ptr(W), step, tau, noise_scale,
+                                                _ptr(dW_bf16), _ptr(w_soft_dbg), _stream(stream)))
+
+
+def gsq_recon_workspace_bytes(n_experts: int, tok_offsets, rows_per_expert: int, cols: int) -> int:
+    arr, p = _offsets(tok_offsets)
+    return lib().gsq_recon_workspace_bytes(n_experts, p, rows_per_expert, cols)
+
+
+def gsq_recon_loss_grad(n_experts: int, tok_offsets, rows_per_expert: int, cols: int, X, XT,
+                        dW_bf16, workspace, RT, G, loss, stream=None, workspace_bytes=None):
+    arr, p = _offsets(tok_offsets)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("gsq_recon_loss_grad",
+           lib().gsq_recon_loss_grad(n_experts, p, rows_per_expert, cols, _ptr(X), _ptr(XT),
+                                     _ptr(dW_bf16), _ptr(workspace), workspace_bytes, _ptr(RT),
+                                     _ptr(G), _ptr(loss), _stream(stream)))
+
+
+def gsq_transpose_tokens(n_experts: int, tok_offsets, cols: int, X, XT, stream=None):
+    arr, p = _offsets(tok_offsets)
+    _check("gsq_transpose_tokens", lib().gsq_transpose_tokens(n_experts, p, cols, _ptr(X),
+                                                              _ptr(XT), _stream(stream)))
+
+
+def gsq_relax_bwd_lion(layer: GsqLayer, G, logits, mom, scales, scale_mom, init_codes,
+                       step: int, tau: float, noise_scale: float, lion: GsqLion,
+                       grad_logits_dbg=None, grad_scales_dbg=None, stream=None):
+    _check("gsq_relax_bwd_lion",
+           lib().gsq_relax_bwd_lion(ctypes.byref(layer), _ptr(G), _ptr(logits), _ptr(mom),
+                                    _ptr(scales), _ptr(scale_mom), _ptr(init_codes), step, tau,
+                                    noise_scale, ctypes.byref(lion), _ptr(grad_logits_dbg),
+                                    _ptr(grad_scales_dbg), _stream(stream)))
+
+
+def gsq_harden_pack(layer: GsqLayer, logits, scales, init_codes, codes=None, packed=None,
+                    scales_f16=None, stream=None):
+    _check("gsq_harden_pack", lib().gsq_harden_pack(ctypes.byref(layer), _ptr(logits),
+                                                    _ptr(scales), _ptr(init_codes), _ptr(codes),
+                                                    _ptr(packed), _ptr(scales_f16),
+                                                    _stream(stream)))
+
+
+def gsq_noise_dump(layer: GsqLayer, step: int, first: int, count: int, out, stream=None):
+    _check("gsq_noise_dump", lib().gsq_noise_dump(ctypes.byref(layer), step, first, count,
+                                                  _ptr(out), _stream(stream)))

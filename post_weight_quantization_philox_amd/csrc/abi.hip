@@ -1,0 +1,257 @@
+// C ABI of the GSQ library: argument checks, then launches on the caller's
+// stream. Every check runs before anything touches the device, so a rejected
+// call has no side effect.
+#include <cmath>
+#include <cstdint>
+
+#include "gsq_internal.hpp"
+
+namespace {
+
+using gsq::LayerDesc;
+
+constexpr int64_t kMaxCoords = int64_t(1) << 40;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int num_logits(int grid) {
+    switch (grid) {
+        case GSQ_GRID_INT2: return 4;
+        case GSQ_GRID_TERNARY: return 2;
+        case GSQ_GRID_INT3_LOCAL: return 5;
+        default: return 0;
+    }
+}
+
+gsq_status check_layer(const gsq_layer* L, LayerDesc* d) {
+    if (L == nullptr) return GSQ_ERR_NULL;
+    if (num_logits(L->grid) == 0) return GSQ_ERR_GRID;
+    if (L->group != 128) return GSQ_ERR_SHAPE;
+    if (L->rows <= 0 || L->cols <= 0 || (L->cols % 128) != 0) return GSQ_ERR_SHAPE;
+    if (L->rows > kMaxCoords / L->cols) return GSQ_ERR_SHAPE;
+    if (L->w_dtype != GSQ_DTYPE_F32 && L->w_dtype != GSQ_DTYPE_BF16) return GSQ_ERR_PARAM;
+    d->grid = L->grid;
+    d->w_bf16 = L->w_dtype == GSQ_DTYPE_BF16;
+    d->rows = static_cast<uint64_t>(L->rows);
+    d->cols = static_cast<uint64_t>(L->cols);
+    d->mk = d->rows * d->cols;
+    d->sid = L->stream;
+    d->key.k0 = static_cast<uint32_t>(L->seed);
+    d->key.k1 = static_cast<uint32_t>(L->seed >> 32);
+    return GSQ_OK;
+}
+
+// A required device tensor: present and 16-byte aligned.
+gsq_status need(const void* p) {
+    if (p == nullptr) return GSQ_ERR_NULL;
+    return aligned16(p) ? GSQ_OK : GSQ_ERR_ALIGN;
+}
+
+// An optional device tensor: NULL, or 16-byte aligned.
+gsq_status maybe(const void* p) { return (p == nullptr || aligned16(p)) ? GSQ_OK : GSQ_ERR_ALIGN; }
+
+gsq_status check_tau(float tau, float noise_scale, gsq::TauK* tk) {
+    if (!std::isfinite(tau) || !(tau > 0.0f)) return GSQ_ERR_PARAM;
+    if (!std::isfinite(noise_scale) || noise_scale < 0.0f || noise_scale > 1.0f) return GSQ_ERR_PARAM;
+    const double inv = 1.0 / static_cast<double>(tau);
+    if (!std::isfinite(inv * 1.4426950408889634)) return GSQ_ERR_PARAM;
+    tk->a = static_cast<float>(1.4426950408889634 * inv);
+    tk->b = static_cast<float>(static_cast<double>(noise_scale) * inv);
+    tk->invtau = static_cast<float>(inv);
+    return GSQ_OK;
+}
+
+gsq_status lion_consts(float lr, const gsq_lion* l, gsq::LionK* k) {
+    if (!std::isfinite(lr) || lr < 0.0f) return GSQ_ERR_PARAM;
+    if (!(l->beta1 >= 0.0f && l->beta1 < 1.0f) || !(l->beta2 >= 0.0f && l->beta2 < 1.0f))
+        return GSQ_ERR_PARAM;
+    if (!std::isfinite(l->weight_decay) || l->weight_decay < 0.0f) return GSQ_ERR_PARAM;
+    k->lr = lr;
+    k->b1 = l->beta1;
+    k->omb1 = 1.0f - l->beta1;
+    k->b2 = l->beta2;
+    k->omb2 = 1.0f - l->beta2;
+    k->wd = l->weight_decay;
+    return GSQ_OK;
+}
+
+#define GSQ_TRY(expr)                         \
+    do {                                      \
+        const gsq_status s_ = (expr);         \
+        if (s_ != GSQ_OK) return s_;          \
+    } while (0)
+
+inline gsq_status hip_status(hipError_t e) { return e == hipSuccess ? GSQ_OK : GSQ_ERR_HIP; }
+
+gsq_status check_offsets(int32_t n_experts, const int64_t* offs, int64_t rows_per_expert,
+                         int64_t cols) {
+    if (n_experts < 1) return GSQ_ERR_SHAPE;
+    if (offs == nullptr) return GSQ_ERR_NULL;
+    if (rows_per_expert <= 0 || rows_per_expert > INT32_MAX) return GSQ_ERR_SHAPE;
+    if (cols <= 0 || (cols % 128) != 0 || cols > INT32_MAX) return GSQ_ERR_SHAPE;
+    if (offs[0] != 0) return GSQ_ERR_SHAPE;
+    for (int e = 0; e < n_experts; ++e) {
+        const int64_t ne = offs[e + 1] - offs[e];
+        if (ne < 0 || (offs[e + 1] % 64) != 0 || ne > INT32_MAX) return GSQ_ERR_SHAPE;
+    }
+    if (offs[n_experts] > kMaxCoords / cols) return GSQ_ERR_SHAPE;
+    if (static_cast<int64_t>(n_experts) * rows_per_expert > kMaxCoords / cols) return GSQ_ERR_SHAPE;
+    return GSQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gsq_abi_version(void) { return GSQ_ABI_VERSION; }
+
+const char* gsq_status_str(int status) {
+    switch (status) {
+        case GSQ_OK: return "GSQ_OK";
+        case GSQ_ERR_NULL: return "GSQ_ERR_NULL";
+        case GSQ_ERR_SHAPE: return "GSQ_ERR_SHAPE";
+        case GSQ_ERR_ALIGN: return "GSQ_ERR_ALIGN";
+        case GSQ_ERR_GRID: return "GSQ_ERR_GRID";
+        case GSQ_ERR_PARAM: return "GSQ_ERR_PARAM";
+        case GSQ_ERR_HIP: return "GSQ_ERR_HIP";
+        default: return "GSQ_ERR_UNKNOWN";
+    }
+}
+
+int gsq_num_logits(int grid) { return num_logits(grid); }
+
+gsq_status gsq_init_rtn(const gsq_layer* layer, const void* W, float* scales, uint8_t* codes,
+                        float* logits, float init_logit, void* stream) {
+    LayerDesc d;
+    GSQ_TRY(check_layer(layer, &d));
+    GSQ_TRY(need(W));
+    GSQ_TRY(need(scales));
+    GSQ_TRY(need(codes));
+    GSQ_TRY(need(logits));
+    if (!std::isfinite(init_logit)) return GSQ_ERR_PARAM;
+    return hip_status(gsq::launch_init_rtn(d, W, scales, codes, logits, init_logit,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_relax_fwd(const gsq_layer* layer, const float* logits, const float* scales,
+                         const uint8_t* init_codes, const void* W, uint32_t step, float tau,
+                         float noise_scale, uint16_t* dW_bf16, float* w_soft_dbg, void* stream) {
+    LayerDesc d;
+    GSQ_TRY(check_layer(layer, &d));
+    GSQ_TRY(need(logits));
+    GSQ_TRY(need(scales));
+    GSQ_TRY(need(W));
+    GSQ_TRY(need(dW_bf16));
+    GSQ_TRY(maybe(w_soft_dbg));
+    if (d.grid == GSQ_GRID_INT3_LOCAL) {
+        if (init_codes == nullptr) return GSQ_ERR_GRID;
+        GSQ_TRY(need(init_codes));
+    }
+    gsq::TauK tk;
+    GSQ_TRY(check_tau(tau, noise_scale, &tk));
+    return hip_status(gsq::launch_relax_fwd(d, logits, scales, init_codes, W, step, tk, dW_bf16,
+                                            w_soft_dbg, static_cast<hipStream_t>(stream)));
+}
+
+size_t gsq_recon_workspace_bytes(int32_t n_experts, const int64_t* tok_offsets,
+                                 int64_t rows_per_expert, int64_t cols) {
+    if (check_offsets(n_experts, tok_offsets, rows_per_expert, cols) != GSQ_OK) return 0;
+    const size_t n = gsq::recon_partials(n_experts, tok_offsets, rows_per_expert);
+    return ((n * sizeof(float) + 255) / 256) * 256 + 256;
+}
+
+gsq_status gsq_recon_loss_grad(int32_t n_experts, const int64_t* tok_offsets,
+                               int64_t rows_per_expert, int64_t cols, const uint16_t* X,
+                               const uint16_t* XT, const uint16_t* dW_bf16, void* workspace,
+                               size_t workspace_bytes, uint16_t* RT, float* G, double* loss,
+                               void* stream) {
+    GSQ_TRY(check_offsets(n_experts, tok_offsets, rows_per_expert, cols));
+    const bool any_tokens = tok_offsets[n_experts] > 0;
+    if (any_tokens) {
+        GSQ_TRY(need(X));
+        GSQ_TRY(need(XT));
+        GSQ_TRY(need(RT));
+    }
+    GSQ_TRY(need(dW_bf16));
+    GSQ_TRY(need(workspace));
+    GSQ_TRY(need(G));
+    GSQ_TRY(need(loss));
+    if (workspace_bytes < gsq_recon_workspace_bytes(n_experts, tok_offsets, rows_per_expert, cols))
+        return GSQ_ERR_SHAPE;
+    return hip_status(gsq::launch_recon(n_experts, tok_offsets, rows_per_expert, cols, X, XT,
+                                        dW_bf16, static_cast<float*>(workspace), RT, G, loss,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets, int64_t cols,
+                                const uint16_t* X, uint16_t* XT, void* stream) {
+    GSQ_TRY(check_offsets(n_experts, tok_offsets, 1, cols));
+    if (tok_offsets[n_experts] == 0) return GSQ_OK;
+    GSQ_TRY(need(X));
+    GSQ_TRY(need(XT));
+    return hip_status(gsq::launch_transpose_tokens(n_experts, tok_offsets, cols, X, XT,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_relax_bwd_lion(const gsq_layer* layer, const float* G, float* logits, float* mom,
+                              float* scales, float* scale_mom, const uint8_t* init_codes,
+                              uint32_t step, float tau, float noise_scale, const gsq_lion* lion,
+                              float* grad_logits_dbg, float* grad_scales_dbg, void* stream) {
+    LayerDesc d;
+    GSQ_TRY(check_layer(layer, &d));
+    GSQ_TRY(need(G));
+    GSQ_TRY(need(logits));
+    GSQ_TRY(need(mom));
+    GSQ_TRY(need(scales));
+    GSQ_TRY(need(scale_mom));
+    GSQ_TRY(maybe(grad_logits_dbg));
+    GSQ_TRY(maybe(grad_scales_dbg));
+    if ((grad_logits_dbg == nullptr) != (grad_scales_dbg == nullptr)) return GSQ_ERR_NULL;
+    if (d.grid == GSQ_GRID_INT3_LOCAL) {
+        if (init_codes == nullptr) return GSQ_ERR_GRID;
+        GSQ_TRY(need(init_codes));
+    }
+    if (lion == nullptr) return GSQ_ERR_NULL;
+    gsq::TauK tk;
+    GSQ_TRY(check_tau(tau, noise_scale, &tk));
+    gsq::LionK lkl, lks;
+    GSQ_TRY(lion_consts(lion->lr_logit, lion, &lkl));
+    GSQ_TRY(lion_consts(lion->lr_scale, lion, &lks));
+    return hip_status(gsq::launch_relax_bwd_lion(d, G, logits, mom, scales, scale_mom, init_codes,
+                                                 step, tk, lkl, lks, grad_logits_dbg,
+                                                 grad_scales_dbg, static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_harden_pack(const gsq_layer* layer, const float* logits, const float* scales,
+                           const uint8_t* init_codes, uint8_t* codes, uint32_t* packed,
+                           uint16_t* scales_f16, void* stream) {
+    LayerDesc d;
+    GSQ_TRY(check_layer(layer, &d));
+    GSQ_TRY(need(logits));
+    GSQ_TRY(maybe(codes));
+    GSQ_TRY(maybe(packed));
+    GSQ_TRY(maybe(scales_f16));
+    if (scales_f16 != nullptr) GSQ_TRY(need(scales));
+    if (d.grid == GSQ_GRID_INT3_LOCAL) {
+        if (init_codes == nullptr) return GSQ_ERR_GRID;
+        GSQ_TRY(need(init_codes));
+    }
+    if (codes == nullptr && packed == nullptr && scales_f16 == nullptr) return GSQ_OK;
+    return hip_status(gsq::launch_harden_pack(d, logits, scales, init_codes, codes, packed,
+                                              scales_f16, static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_noise_dump(const gsq_layer* layer, uint32_t step, int64_t first, int64_t count,
+                          uint32_t* out, void* stream) {
+    LayerDesc d;
+    GSQ_TRY(check_layer(layer, &d));
+    if (first < 0 || count < 0) return GSQ_ERR_SHAPE;
+    if (count == 0) return GSQ_OK;
+    if (out == nullptr) return GSQ_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0) return GSQ_ERR_ALIGN;
+    return hip_status(gsq::launch_noise_dump(d, step, static_cast<uint64_t>(first),
+                                             static_cast<uint64_t>(count), out,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

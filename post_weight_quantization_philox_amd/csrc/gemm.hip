@@ -1,0 +1,351 @@
+// Reconstruction contractions of the GSQ step on the gfx950 matrix cores.
+//
+// Both products are "NT": C[i][j] = alpha * sum_r A[i][r] * B[j][r] with the
+// contraction index r contiguous in both operands.
+//   GEMM1  R^T = dW X^T      A = dW [M][K],   B = X   [N][K]  -> R^T [M][N] bf16,
+//                            plus the per-tile partial sum of R^2 (the loss);
+//   GEMM2  G   = 2 R^T X     A = R^T [M][N],  B = X^T [K][N]  -> G [M][K] fp32.
+//
+// Tiling: 256x256 output tile per workgroup of 4 waves (2x2), each wave a
+// 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 blocks (256 fp32
+// accumulators per lane). K advances 64 at a time through two LDS buffers
+// (2 x 64 KiB): global loads for step k+1 are in flight while step k's
+// fragments are read from LDS. LDS rows are 128 bytes; the 16-byte chunk
+// index is XOR-swizzled with the row so both the stores (8 threads per row)
+// and the fragment reads (32 rows x 16 bytes per half-wave) are free of bank
+// conflicts. Workgroups are renumbered so that consecutive tiles share an XCD
+// (the dispatcher deals workgroups round-robin over the 8 XCDs) and tiles are
+// ordered in groups of 4 tile-rows, which keeps each XCD's A and B panels in
+// its own L2.
+#include "gsq_internal.hpp"
+
+namespace gsq {
+
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NT = 256;
+constexpr int kChunks = BK / 8;   // 16-byte chunks per tile row
+constexpr int kGroupM = 4;
+// Byte offset past every operand buffer (their sizes are checked to stay below
+// it), so a load there is out of range and returns zeros.
+constexpr uint32_t kOob = 0x7FFFFF00u;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+enum { EPI_BF16_LOSS = 0, EPI_F32_SCALED = 1 };
+
+struct GemmArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    int64_t lda, ldb, ldc;
+    int I, J, Rd;
+    int a_bytes, b_bytes;   // operand buffer sizes for the range check
+    int tiles_i, tiles_j;
+    void* C;
+    float alpha;
+    float* partials;   // EPI_BF16_LOSS: one float per workgroup
+};
+
+__device__ __forceinline__ void tile_of(const GemmArgs& g, int& ti, int& tj) {
+    const int nwg = gridDim.x;
+    const int wg = blockIdx.x;
+    int logical = wg;
+    if ((nwg & 7) == 0) logical = (wg & 7) * (nwg >> 3) + (wg >> 3);
+    const int width = kGroupM * g.tiles_j;
+    const int grp = logical / width;
+    const int first = grp * kGroupM;
+    const int gm = min(g.tiles_i - first, kGroupM);
+    const int in = logical - grp * width;
+    ti = first + in % gm;
+    tj = in / gm;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One K-step of one operand tile: 256 rows x 64 bf16 = 32 KiB, written by
+// direct global->LDS loads. Wave w, load q fills tile rows R0..R0+7 with
+// R0 = 8*(4q + w); lane l lands at LDS row R0 + l/8, physical chunk l%8, and
+// therefore fetches logical chunk (l%8) ^ (row & 7) of its row (the swizzle).
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[8], uint32_t koff,
+                                         uint4* tile, int wave) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int r0 = 8 * (4 * q + wave);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + r0 * kChunks), 16,
+                                                 off[q] + koff, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int EPI>
+__global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
+    __shared__ uint4 sA0[BM * kChunks];
+    __shared__ uint4 sB0[BN * kChunks];
+    __shared__ uint4 sA1[BM * kChunks];
+    __shared__ uint4 sB1[BN * kChunks];
+
+    int ti, tj;
+    tile_of(g, ti, tj);
+    const int i0 = ti * BM, j0 = tj * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wi = wave >> 1, wj = wave & 1;
+
+    // Per-lane byte offsets of the rows this lane fetches. Rows past the edge
+    // get an offset beyond the buffer: the hardware range check returns zeros.
+    const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(g.A), 0, g.a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(g.B), 0, g.b_bytes, 0x00020000);
+    const int lrow = lane >> 3;
+    const int lch = (lane & 7) ^ (lrow & 7);
+    uint32_t oa[8], ob[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = 8 * (4 * q + wave) + lrow;
+        const int rowa = i0 + row, rowb = j0 + row;
+        oa[q] = rowa < g.I ? static_cast<uint32_t>((static_cast<int64_t>(rowa) * g.lda + lch * 8) * 2) : kOob;
+        ob[q] = rowb < g.J ? static_cast<uint32_t>((static_cast<int64_t>(rowb) * g.ldb + lch * 8) * 2) : kOob;
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    // Fragment addressing: lane reads row (lane & 31) of a 32-row block, chunk
+    // 2*kk + (lane >> 5) of the 64-wide K slice; block rows are multiples of
+    // 8, so the swizzle term is (lane & 7).
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+    const int fsw = lane & 7;
+    const int rowA = wi * 128 + frow;
+    const int rowB = wj * 128 + frow;
+
+    auto compute = [&](const uint4* tA, const uint4* tB) {
+        bf16x8 fa[2][4], fb[2][4];
+        auto fetch = [&](int kk, int slot) {
+            const int ch = (2 * kk + fhalf) ^ fsw;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                fa[slot][b] = __builtin_bit_cast(bf16x8, tA[(rowA + 32 * b) * kChunks + ch]);
+                fb[slot][b] = __builtin_bit_cast(bf16x8, tB[(rowB + 32 * b) * kChunks + ch]);
+            }
+        };
+        fetch(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            // The next slice's fragments are requested before this slice's 16
+            // MFMAs so the LDS latency hides behind them; the scheduling
+            // barriers keep the compiler from sinking the reads to their uses.
+            if (kk + 1 < 4) fetch(kk + 1, (kk + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][a], fb[kk & 1][b],
+                                                                        acc[a][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int nk = g.Rd / BK;
+    constexpr uint32_t kStep = BK * 2;   // bytes of one K-step along a row
+    dma_tile(ra_rs, oa, 0, sA0, wave);
+    dma_tile(rb_rs, ob, 0, sB0, wave);
+    wait_dma();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool odd = kt & 1;
+        if (kt + 1 < nk) {
+            dma_tile(ra_rs, oa, (kt + 1) * kStep, odd ? sA0 : sA1, wave);
+            dma_tile(rb_rs, ob, (kt + 1) * kStep, odd ? sB0 : sB1, wave);
+        }
+        compute(odd ? sA1 : sA0, odd ? sB1 : sB0);
+        wait_dma();
+        __syncthreads();
+    }
+
+    // Epilogue, one 32-row slab of the wave's 128x128 sub-tile at a time:
+    // accumulators go to a private 32x128 fp32 LDS slab (register r of block
+    // (a, b) is C[8*(r/4) + 4*(lane/32) + r%4][32*b + lane%32]), then each
+    // lane reads back 8 consecutive values of one row and stores them as one
+    // 16-byte (bf16) or two 16-byte (fp32) vectors. N and K are multiples of
+    // 8, so a vector is entirely inside or outside the matrix.
+    float* slab = reinterpret_cast<float*>(wave < 2 ? sA0 : sB0) + (wave & 1) * (32 * 128);
+    const int grow0 = i0 + wi * 128;
+    const int gcol0 = j0 + wj * 128;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + 4 * fhalf + (r & 3);
+                slab[row * 128 + 32 * b + frow] = acc[a][b][r];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int c = lane + 64 * t;          // 512 chunks of 8 values
+            const int row = c >> 4, col = (c & 15) * 8;
+            const float4 v0 = *reinterpret_cast<const float4*>(slab + row * 128 + col);
+            const float4 v1 = *reinterpret_cast<const float4*>(slab + row * 128 + col + 4);
+            const int grow = grow0 + a * 32 + row, gcol = gcol0 + col;
+            if (grow < g.I && gcol < g.J) {
+                const int64_t off = static_cast<int64_t>(grow) * g.ldc + gcol;
+                if constexpr (EPI == EPI_BF16_LOSS) {
+                    lsum = __builtin_fmaf(v0.x, v0.x, lsum); lsum = __builtin_fmaf(v0.y, v0.y, lsum);
+                    lsum = __builtin_fmaf(v0.z, v0.z, lsum); lsum = __builtin_fmaf(v0.w, v0.w, lsum);
+                    lsum = __builtin_fmaf(v1.x, v1.x, lsum); lsum = __builtin_fmaf(v1.y, v1.y, lsum);
+                    lsum = __builtin_fmaf(v1.z, v1.z, lsum); lsum = __builtin_fmaf(v1.w, v1.w, lsum);
+                    uint4 o;
+                    o.x = pack_bf16x2(v0.x, v0.y); o.y = pack_bf16x2(v0.z, v0.w);
+                    o.z = pack_bf16x2(v1.x, v1.y); o.w = pack_bf16x2(v1.z, v1.w);
+                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C) + off) = o;
+                } else {
+                    float* dst = static_cast<float*>(g.C) + off;
+                    *reinterpret_cast<float4*>(dst) =
+                        make_float4(g.alpha * v0.x, g.alpha * v0.y, g.alpha * v0.z, g.alpha * v0.w);
+                    *reinterpret_cast<float4*>(dst + 4) =
+                        make_float4(g.alpha * v1.x, g.alpha * v1.y, g.alpha * v1.z, g.alpha * v1.w);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if constexpr (EPI == EPI_BF16_LOSS) {
+        // Fixed-order reduction: wave butterfly, then waves 0..3 in order.
+        __shared__ float red[NT / 64];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) lsum += __shfl_xor(lsum, m, 64);
+        if (lane == 0) red[wave] = lsum;
+        __syncthreads();
+        if (tid == 0) g.partials[blockIdx.x] = ((red[0] + red[1]) + red[2]) + red[3];
+    }
+}
+
+__global__ __launch_bounds__(256) void loss_finalize_kernel(const float* __restrict__ partials,
+                                                            int n, double* __restrict__ loss) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n; i += 256) s += static_cast<double>(partials[i]);
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *loss = red[0];
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// X [n][cols] -> XT [cols][n], 64x64 tiles through LDS (n % 64 == 0,
+// cols % 64 == 0).
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ X,
+                                                        uint16_t* __restrict__ XT, int64_t n,
+                                                        int64_t cols) {
+    __shared__ uint16_t t[64][66];
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int r = ty; r < 64; r += 4) t[r][tx] = X[(r0 + r) * cols + c0 + tx];
+    __syncthreads();
+    for (int c = ty; c < 64; c += 4) XT[(c0 + c) * n + r0 + tx] = t[tx][c];
+}
+
+inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+template <int EPI>
+hipError_t run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int I, int J,
+                    int Rd, void* C, int64_t ldc, float alpha, float* partials, hipStream_t st) {
+    GemmArgs g;
+    g.A = A; g.B = B; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+    g.I = I; g.J = J; g.Rd = Rd;
+    const int64_t ab = static_cast<int64_t>(I) * lda * 2, bb = static_cast<int64_t>(J) * ldb * 2;
+    // Valid offsets plus the largest K offset stay below kOob, and kOob plus
+    // that offset stays below 2^32, so the range check separates the two.
+    if (Rd <= 0 || Rd % BK != 0 || ab > static_cast<int64_t>(kOob) - 2 * static_cast<int64_t>(Rd) ||
+        bb > static_cast<int64_t>(kOob) - 2 * static_cast<int64_t>(Rd))
+        return hipErrorInvalidValue;
+    g.a_bytes = static_cast<int>(ab);
+    g.b_bytes = static_cast<int>(bb);
+    g.tiles_i = cdiv(I, BM); g.tiles_j = cdiv(J, BN);
+    g.C = C; g.alpha = alpha; g.partials = partials;
+    const int nwg = g.tiles_i * g.tiles_j;
+    hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3(nwg), dim3(NT), 0, st, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t recon_partials(int32_t n_experts, const int64_t* tok_offsets, int64_t rows_per_expert) {
+    size_t n = 0;
+    for (int e = 0; e < n_experts; ++e) {
+        const int64_t ne = tok_offsets[e + 1] - tok_offsets[e];
+        if (ne > 0) n += static_cast<size_t>(cdiv(rows_per_expert, BM)) * cdiv(ne, BN);
+    }
+    return n;
+}
+
+hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t rows_per_expert,
+                        int64_t cols, const uint16_t* X, const uint16_t* XT, const uint16_t* dW,
+                        float* partials, uint16_t* RT, float* G, double* loss, hipStream_t st) {
+    size_t slot = 0;
+    hipError_t err = hipSuccess;
+    for (int e = 0; e < n_experts && err == hipSuccess; ++e) {
+        const int64_t t0 = tok_offsets[e];
+        const int64_t ne = tok_offsets[e + 1] - t0;
+        const uint16_t* dWe = dW + static_cast<int64_t>(e) * rows_per_expert * cols;
+        float* Ge = G + static_cast<int64_t>(e) * rows_per_expert * cols;
+        if (ne == 0) {
+            const int64_t n = rows_per_expert * cols;
+            hipLaunchKernelGGL(fill_zero_kernel, dim3(cdiv(n, 256)), dim3(256), 0, st, Ge, n);
+            err = hipGetLastError();
+            continue;
+        }
+        uint16_t* RTe = RT + rows_per_expert * t0;
+        err = run_gemm<EPI_BF16_LOSS>(dWe, cols, X + t0 * cols, cols, static_cast<int>(rows_per_expert),
+                                      static_cast<int>(ne), static_cast<int>(cols), RTe, ne, 1.0f,
+                                      partials + slot, st);
+        if (err != hipSuccess) break;
+        slot += static_cast<size_t>(cdiv(rows_per_expert, BM)) * cdiv(ne, BN);
+        err = run_gemm<EPI_F32_SCALED>(RTe, ne, XT + cols * t0, ne, static_cast<int>(rows_per_expert),
+                                       static_cast<int>(cols), static_cast<int>(ne), Ge, cols, 2.0f,
+                                       nullptr, st);
+    }
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(256), 0, st, partials,
+                       static_cast<int>(slot), loss);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets, int64_t cols,
+                                   const uint16_t* X, uint16_t* XT, hipStream_t st) {
+    for (int e = 0; e < n_experts; ++e) {
+        const int64_t t0 = tok_offsets[e];
+        const int64_t ne = tok_offsets[e + 1] - t0;
+        if (ne == 0) continue;
+        hipLaunchKernelGGL(transpose_kernel, dim3(cdiv(cols, 64), cdiv(ne, 64)), dim3(256), 0, st,
+                           X + t0 * cols, XT + cols * t0, ne, cols);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+}  // namespace gsq

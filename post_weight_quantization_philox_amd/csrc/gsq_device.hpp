@@ -1,0 +1,138 @@
+// Device helpers shared by the GSQ kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gsq {
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11), written from the
+// published round function: the products M0*c0 and M1*c2 (32x32 -> 64 bit),
+// new counter (hi1^c1^k0, lo1, hi0^c3^k1, lo0), key bumped by the Weyl
+// constants between rounds. The key is wave-uniform, so its schedule stays in
+// scalar registers; each round costs two v_mad_u64_u32 and two xor3.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+struct Key { uint32_t k0, k1; };
+
+__device__ __forceinline__ void philox_block(uint64_t blk, uint32_t step, uint32_t sid,
+                                             Key key, uint32_t out[4]) {
+    uint32_t c0 = static_cast<uint32_t>(blk);
+    uint32_t c1 = static_cast<uint32_t>(blk >> 32);
+    uint32_t c2 = step;
+    uint32_t c3 = sid;
+    uint32_t k0 = key.k0, k1 = key.k1;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c0;
+        const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c2;
+        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+        c1 = static_cast<uint32_t>(p1);
+        c3 = static_cast<uint32_t>(p0);
+        c0 = n0;
+        c2 = n2;
+        k0 += kPhiloxW0;
+        k1 += kPhiloxW1;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+// Noise words of the four coordinates i0..i0+3 (i0 % 4 == 0) of a grid with L
+// logits: stream elements e = i*L + k, i.e. the L whole blocks starting at
+// block i0*L/4. Word c*L + k belongs to coordinate i0 + c, logit k.
+template <int L>
+__device__ __forceinline__ void noise_words4(uint64_t i0, uint32_t step, uint32_t sid, Key key,
+                                             uint32_t w[4 * L]) {
+    const uint64_t b0 = (i0 >> 2) * L;
+#pragma unroll
+    for (int j = 0; j < L; ++j) philox_block(b0 + j, step, sid, key, &w[4 * j]);
+}
+
+// Uniform in (0,1): top 24 bits forced odd, times 2^-24 (exact in fp32).
+__device__ __forceinline__ float uniform24(uint32_t x) {
+    return static_cast<float>((x >> 8) | 1u) * 0x1p-24f;
+}
+
+// Hardware base-2 logarithm and exponential (v_log_f32 / v_exp_f32). Their
+// arguments here are never denormal: uniforms are >= 2^-24 and -log2(u) is
+// >= 8.6e-8.
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Gumbel noise in base-2 units up to a constant: a standard Gumbel g equals
+// -ln(-ln u) = -ln2 * (log2(-log2 u) + log2(ln 2)), so g*log2(e) =
+// -log2(-log2 u) - log2(ln 2). The constant is the same for every logit of a
+// coordinate and cancels in the softmax, so kernels use t = log2(-log2 u) and
+// form y_k = (l_k*log2e - eta*t_k)/tau.
+__device__ __forceinline__ float gumbel_t(uint32_t word) {
+    return hw_log2(-hw_log2(uniform24(word)));
+}
+
+// Standard logistic noise in base-2 units: n*log2(e) = log2(u) - log2(1-u)
+// (1-u is exact in fp32 for the 24-bit uniforms).
+__device__ __forceinline__ float logistic_b2(uint32_t word) {
+    const float u = uniform24(word);
+    return hw_log2(u) - hw_log2(1.0f - u);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Conversions
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    _Float16 h = static_cast<_Float16>(x);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// ---------------------------------------------------------------------------
+// Reductions within the 32 lanes that share a scale group (lanes 0-31 and
+// 32-63 of a wave hold two different groups). Butterfly: every lane ends with
+// the full result; callers let one fixed lane write it, so the stored value is
+// deterministic.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float group32_sum(float v) {
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ float group32_max(float v) {
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+// Lion on one fp32 parameter (Chen et al. 2023). The sign is taken on
+// c = fma(beta1, m, fp32((1-beta1)*g)); theta -= lr*(sign(c) + wd*theta);
+// m = fma(beta2, m, fp32((1-beta2)*g)).
+struct LionK {
+    float lr, b1, omb1, b2, omb2, wd;
+};
+
+__device__ __forceinline__ void lion_update(float& theta, float& m, float g, const LionK& k) {
+    const float c = __builtin_fmaf(k.b1, m, __fmul_rn(k.omb1, g));
+    const float sgn = (c > 0.0f) ? 1.0f : ((c < 0.0f) ? -1.0f : 0.0f);
+    theta = __builtin_fmaf(-k.lr, __builtin_fmaf(k.wd, theta, sgn), theta);
+    m = __builtin_fmaf(k.b2, m, __fmul_rn(k.omb2, g));
+}
+
+}  // namespace gsq

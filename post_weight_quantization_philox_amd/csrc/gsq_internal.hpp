@@ -1,0 +1,52 @@
+// Launchers shared between the kernel files and the C ABI (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gsq.h"
+#include "gsq_device.hpp"
+
+namespace gsq {
+
+struct LayerDesc {
+    int grid;
+    bool w_bf16;
+    uint64_t rows, cols, mk;  // mk = rows * cols
+    uint32_t sid;
+    Key key;
+};
+
+// Per-launch temperature constants: y = l*a - b*t (Gumbel) or l*a + b*n2
+// (logistic), with a = log2(e)/tau, b = eta/tau.
+struct TauK {
+    float a, b, invtau;
+};
+
+hipError_t launch_init_rtn(const LayerDesc& d, const void* W, float* scales, uint8_t* codes,
+                           float* logits, float init_logit, hipStream_t st);
+hipError_t launch_relax_fwd(const LayerDesc& d, const float* logits, const float* scales,
+                            const uint8_t* codes, const void* W, uint32_t step, TauK tk,
+                            uint16_t* dW, float* w_soft_dbg, hipStream_t st);
+hipError_t launch_relax_bwd_lion(const LayerDesc& d, const float* G, float* logits, float* mom,
+                                 float* scales, float* scale_mom, const uint8_t* codes,
+                                 uint32_t step, TauK tk, LionK lk_logit, LionK lk_scale,
+                                 float* grad_logits_dbg, float* grad_scales_dbg, hipStream_t st);
+hipError_t launch_harden_pack(const LayerDesc& d, const float* logits, const float* scales,
+                              const uint8_t* codes, uint8_t* codes_out, uint32_t* packed,
+                              uint16_t* scales_f16, hipStream_t st);
+hipError_t launch_noise_dump(const LayerDesc& d, uint32_t step, uint64_t first, uint64_t count,
+                             uint32_t* out, hipStream_t st);
+
+// Reconstruction GEMMs.
+struct ExpertSpan {
+    int64_t tok0, ntok;  // token block of the expert (multiple of 64)
+};
+size_t recon_partials(int32_t n_experts, const int64_t* tok_offsets, int64_t rows_per_expert);
+hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t rows_per_expert,
+                        int64_t cols, const uint16_t* X, const uint16_t* XT, const uint16_t* dW,
+                        float* partials, uint16_t* RT, float* G, double* loss, hipStream_t st);
+hipError_t launch_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets, int64_t cols,
+                                   const uint16_t* X, uint16_t* XT, hipStream_t st);
+
+}  // namespace gsq

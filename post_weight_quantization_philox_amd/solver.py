@@ -1,0 +1,145 @@
+"""Per-layer GSQ solve driven from the host: device state plus the call order.
+
+PyTorch only allocates the device tensors and provides the stream; every
+arithmetic step runs in ``libgsq.so``. One :class:`LayerSolver` holds the
+state of one layer (or one batch of experts) for the whole annealed solve:
+
+* logits and their Lion momentum, planar [L][rows][cols] fp32;
+* group scales and their momentum, [rows][cols/128] fp32;
+* warm-start codes, [rows][cols] uint8;
+* dW (bf16), G (fp32), R^T (bf16) and the loss partial workspace;
+* the calibration tokens X (bf16) and their per-expert transpose X^T.
+
+Memory per coordinate: 8L bytes of logits + momentum, 1 (codes), 2 (dW),
+4 (G), plus W itself; R^T, X and X^T scale with the token count.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import (GRID_INT3_LOCAL, DTYPE_BF16, DTYPE_F32, N_LOGITS, CODE_BITS, GsqLayer,
+               GsqLion, gsq_init_rtn, gsq_relax_fwd, gsq_recon_workspace_bytes,
+               gsq_recon_loss_grad, gsq_transpose_tokens, gsq_relax_bwd_lion,
+               gsq_harden_pack)
+
+TOKEN_ALIGN = 64
+
+
+def tau_schedule(steps: int, tau0: float = 1.0, tau1: float = 0.05) -> list:
+    """Geometric annealing tau_t = tau0 * (tau1/tau0)**(t/(T-1))."""
+    if steps == 1:
+        return [float(np.float32(tau0))]
+    return [float(np.float32(tau0 * (tau1 / tau0) ** (t / (steps - 1)))) for t in range(steps)]
+
+
+def pad_tokens(X: torch.Tensor, tok_offsets) -> tuple:
+    """Pad every expert's token block with zero rows to a multiple of 64.
+
+    A zero token row adds nothing to the reconstruction loss or its gradient,
+    so the padded problem has exactly the same loss and G.
+    """
+    offs = [int(o) for o in tok_offsets]
+    counts = [offs[e + 1] - offs[e] for e in range(len(offs) - 1)]
+    padded = [int(math.ceil(c / TOKEN_ALIGN) * TOKEN_ALIGN) for c in counts]
+    if padded == counts:
+        return X.contiguous(), np.asarray(offs, dtype=np.int64)
+    new_offs = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+    Xp = torch.zeros((int(new_offs[-1]), X.shape[1]), dtype=X.dtype, device=X.device)
+    for e, c in enumerate(counts):
+        Xp[int(new_offs[e]):int(new_offs[e]) + c] = X[offs[e]:offs[e] + c]
+    return Xp, new_offs
+
+
+class LayerSolver:
+    """Device state and step sequence of one layer (or expert batch)."""
+
+    def __init__(self, W: torch.Tensor, X: torch.Tensor, grid: int, tok_offsets=None,
+                 rows_per_expert: int | None = None, seed: int = 0, stream_id: int = 0,
+                 lion: GsqLion | None = None, init_logit: float = 2.0):
+        if not (W.is_cuda and X.is_cuda):
+            raise ValueError("W and X must be device tensors")
+        if W.dtype not in (torch.bfloat16, torch.float32) or X.dtype != torch.bfloat16:
+            raise ValueError("W must be bf16 or fp32 and X bf16")
+        dev = W.device
+        self.W = W.contiguous()
+        self.rows, self.cols = self.W.shape
+        self.grid = grid
+        self.L = N_LOGITS[grid]
+        if tok_offsets is None:
+            tok_offsets = [0, X.shape[0]]
+        self.n_experts = len(tok_offsets) - 1
+        self.rows_per_expert = rows_per_expert or self.rows // self.n_experts
+        if self.rows_per_expert * self.n_experts != self.rows:
+            raise ValueError("rows must equal n_experts * rows_per_expert")
+        self.X, self.tok_offsets = pad_tokens(X, tok_offsets)
+        self.tokens = int(self.tok_offsets[-1])
+        self.layer = GsqLayer.make(grid, self.rows, self.cols,
+                                   DTYPE_BF16 if W.dtype == torch.bfloat16 else DTYPE_F32,
+                                   seed=seed, stream=stream_id)
+        self.lion = lion or GsqLion.make()
+        M, K, L = self.rows, self.cols, self.L
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.logits = torch.empty((L, M, K), **f32)
+        self.mom = torch.zeros((L, M, K), **f32)
+        self.scales = torch.empty((M, K // 128), **f32)
+        self.scale_mom = torch.zeros((M, K // 128), **f32)
+        self.codes = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        self.dW = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        self.G = torch.empty((M, K), **f32)
+        self.RT = torch.empty((max(1, self.rows_per_expert * self.tokens),), dtype=torch.bfloat16,
+                              device=dev)
+        self.XT = torch.empty((max(1, self.tokens * K),), dtype=torch.bfloat16, device=dev)
+        ws = gsq_recon_workspace_bytes(self.n_experts, self.tok_offsets, self.rows_per_expert, K)
+        self.workspace = torch.empty((max(ws, 256) // 4,), **f32)
+        self.loss = torch.zeros((1,), dtype=torch.float64, device=dev)
+        gsq_init_rtn(self.layer, self.W, self.scales, self.codes, self.logits, init_logit)
+        gsq_transpose_tokens(self.n_experts, self.tok_offsets, K, self.X, self.XT)
+
+    @property
+    def init_codes(self):
+        return self.codes if self.grid == GRID_INT3_LOCAL else None
+
+    def relax_fwd(self, step: int, tau: float, noise_scale: float = 1.0, w_soft_dbg=None):
+        gsq_relax_fwd(self.layer, self.logits, self.scales, self.init_codes, self.W, step, tau,
+                      noise_scale, self.dW, w_soft_dbg)
+
+    def recon(self):
+        gsq_recon_loss_grad(self.n_experts, self.tok_offsets, self.rows_per_expert, self.cols,
+                            self.X, self.XT, self.dW, self.workspace, self.RT, self.G, self.loss)
+
+    def relax_bwd_lion(self, step: int, tau: float, noise_scale: float = 1.0,
+                       grad_logits_dbg=None, grad_scales_dbg=None):
+        gsq_relax_bwd_lion(self.layer, self.G, self.logits, self.mom, self.scales, self.scale_mom,
+                           self.init_codes, step, tau, noise_scale, self.lion, grad_logits_dbg,
+                           grad_scales_dbg)
+
+    def step(self, step: int, tau: float, noise_scale: float = 1.0):
+        """One relaxed-quantization step: forward, objective, backward + Lion."""
+        self.relax_fwd(step, tau, noise_scale)
+        self.recon()
+        self.relax_bwd_lion(step, tau, noise_scale)
+
+    def harden(self):
+        """Hard codes (uint8), packed codes (int32 words) and fp16 scales."""
+        M, K = self.rows, self.cols
+        dev = self.W.device
+        codes = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        packed = torch.empty((M, K * CODE_BITS[self.grid] // 32), dtype=torch.int32, device=dev)
+        s16 = torch.empty((M, K // 128), dtype=torch.float16, device=dev)
+        gsq_harden_pack(self.layer, self.logits, self.scales, self.init_codes, codes, packed, s16)
+        return codes, packed, s16
+
+    def solve(self, steps: int, tau0: float = 1.0, tau1: float = 0.05, noise_scale: float = 1.0,
+              log_every: int = 0):
+        """The annealed solve; returns the per-step losses (host, every step
+        if ``log_every`` is 1, else only those logged) and the hard result."""
+        losses = []
+        for t, tau in enumerate(tau_schedule(steps, tau0, tau1)):
+            self.step(t, tau, noise_scale)
+            if log_every and (t % log_every == 0 or t == steps - 1):
+                losses.append(float(self.loss.item()))
+        return losses, self.harden()

@@ -1,0 +1,144 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments before touching a device (every
+call here fails validation, so no kernel is launched)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+g = pytest.importorskip("post_weight_quantization_philox_amd")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_GRID, ERR_PARAM = 0, 1, 2, 3, 4, 5
+FAKE = 0x10000          # an aligned address that is never dereferenced
+FAKE_MISALIGNED = 0x10004
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(g.LIB_PATH):
+        pytest.fail("libgsq.so is not built (python -m post_weight_quantization_philox_amd.build)")
+    return g.lib()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gsq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gsq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_entry_point(L):
+    declared = header_functions()
+    assert len(declared) >= 11
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(g.EXPORTS) == declared
+
+
+def test_version_and_names(L):
+    assert g.gsq_abi_version() == 1
+    assert g.gsq_status_str(0) == "GSQ_OK"
+    assert g.gsq_status_str(3) == "GSQ_ERR_ALIGN"
+    assert [g.gsq_num_logits(k) for k in (0, 1, 2, 7)] == [4, 2, 5, 0]
+
+
+def _fwd(layer, **kw):
+    args = dict(logits=FAKE, scales=FAKE, codes=FAKE, W=FAKE, step=0, tau=1.0, eta=1.0, dW=FAKE,
+                dbg=None)
+    args.update(kw)
+    return g.lib().gsq_relax_fwd(ctypes.byref(layer) if layer is not None else None, args["logits"],
+                                 args["scales"], args["codes"], args["W"], args["step"],
+                                 args["tau"], args["eta"], args["dW"], args["dbg"], None)
+
+
+def test_relax_fwd_validation(L):
+    lay = g.GsqLayer.make(g.GRID_INT2, 4, 256)
+    assert _fwd(None) == ERR_NULL
+    assert _fwd(g.GsqLayer.make(9, 4, 256)) == ERR_GRID
+    assert _fwd(g.GsqLayer.make(g.GRID_INT2, 4, 200)) == ERR_SHAPE
+    assert _fwd(g.GsqLayer.make(g.GRID_INT2, 0, 256)) == ERR_SHAPE
+    assert _fwd(g.GsqLayer.make(g.GRID_INT2, 4, 256, group=64)) == ERR_SHAPE
+    assert _fwd(g.GsqLayer.make(g.GRID_INT2, 4, 256, w_dtype=5)) == ERR_PARAM
+    assert _fwd(lay, logits=None) == ERR_NULL
+    assert _fwd(lay, dW=FAKE_MISALIGNED) == ERR_ALIGN
+    assert _fwd(lay, dbg=FAKE_MISALIGNED) == ERR_ALIGN
+    assert _fwd(lay, tau=0.0) == ERR_PARAM
+    assert _fwd(lay, tau=-1.0) == ERR_PARAM
+    assert _fwd(lay, tau=float("nan")) == ERR_PARAM
+    assert _fwd(lay, tau=float("inf")) == ERR_PARAM
+    assert _fwd(lay, eta=1.5) == ERR_PARAM
+    assert _fwd(lay, eta=-0.1) == ERR_PARAM
+    local = g.GsqLayer.make(g.GRID_INT3_LOCAL, 4, 256)
+    assert _fwd(local, codes=None) == ERR_GRID
+
+
+def test_bwd_lion_validation(L):
+    lay = g.GsqLayer.make(g.GRID_TERNARY, 4, 256)
+    f = g.lib().gsq_relax_bwd_lion
+
+    def call(lion, gl=None, gs=None, tau=1.0):
+        return f(ctypes.byref(lay), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, tau, 1.0,
+                 ctypes.byref(lion) if lion is not None else None, gl, gs, None)
+
+    assert call(None) == ERR_NULL
+    assert call(g.GsqLion.make(beta1=1.0)) == ERR_PARAM
+    assert call(g.GsqLion.make(beta2=-0.5)) == ERR_PARAM
+    assert call(g.GsqLion.make(lr_logit=-1e-3)) == ERR_PARAM
+    assert call(g.GsqLion.make(weight_decay=float("nan"))) == ERR_PARAM
+    assert call(g.GsqLion.make(), gl=FAKE) == ERR_NULL          # both debug outputs or neither
+    assert call(g.GsqLion.make(), tau=0.0) == ERR_PARAM
+
+
+def test_recon_validation(L):
+    f = g.lib().gsq_recon_loss_grad
+    offs_bad = np.array([0, 100], dtype=np.int64)        # not a multiple of 64
+    offs = np.array([0, 128], dtype=np.int64)
+    offs_dec = np.array([0, 128, 64], dtype=np.int64)
+    assert f(1, offs_bad.ctypes.data, 64, 256, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert f(2, offs_dec.ctypes.data, 64, 256, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert f(1, offs.ctypes.data, 64, 200, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert f(0, offs.ctypes.data, 64, 256, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert f(1, None, 64, 256, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == ERR_NULL
+    assert f(1, offs.ctypes.data, 64, 256, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert f(1, offs.ctypes.data, 64, 256, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE_MISALIGNED, FAKE, None) == ERR_ALIGN
+    assert f(1, offs.ctypes.data, 64, 256, None, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == ERR_NULL
+    ws = g.gsq_recon_workspace_bytes(1, offs, 64, 256)
+    assert ws >= 4 and ws % 256 == 0
+    assert g.gsq_recon_workspace_bytes(1, offs_bad, 64, 256) == 0
+
+
+def test_harden_and_noise_validation(L):
+    lay = g.GsqLayer.make(g.GRID_INT3_LOCAL, 4, 256)
+    h = g.lib().gsq_harden_pack
+    assert h(ctypes.byref(lay), FAKE, FAKE, None, FAKE, None, None, None) == ERR_GRID
+    assert h(ctypes.byref(lay), None, FAKE, FAKE, FAKE, None, None, None) == ERR_NULL
+    assert h(ctypes.byref(lay), FAKE, FAKE, FAKE, FAKE_MISALIGNED, None, None, None) == ERR_ALIGN
+    assert h(ctypes.byref(lay), FAKE, FAKE, FAKE, None, None, None, None) == OK    # nothing asked
+    n = g.lib().gsq_noise_dump
+    assert n(ctypes.byref(lay), 0, -1, 4, FAKE, None) == ERR_SHAPE
+    assert n(ctypes.byref(lay), 0, 0, 4, None, None) == ERR_NULL
+    assert n(ctypes.byref(lay), 0, 0, 4, 0x10002, None) == ERR_ALIGN
+    assert n(ctypes.byref(lay), 0, 0, 0, None, None) == OK                          # empty
+    i = g.lib().gsq_init_rtn
+    assert i(ctypes.byref(lay), FAKE, FAKE, FAKE, FAKE, ctypes.c_float(float("inf")), None) == ERR_PARAM
+
+
+def test_binding_raises_named_error(L):
+    lay = g.GsqLayer.make(g.GRID_INT2, 4, 200)
+    with pytest.raises(g.GsqError) as e:
+        g.gsq_relax_fwd(lay, FAKE, FAKE, None, FAKE, 0, 1.0, 1.0, FAKE)
+    assert e.value.name == "GSQ_ERR_SHAPE"
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "post_weight_quantization_philox_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), fn
+                assert "oracle/" not in text, fn
