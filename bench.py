@@ -1,0 +1,204 @@
+"""Throughput of the GSQ relaxed-quantization step on one MI355X.
+
+A step is one pass of the whole hot path over the layer: relaxed forward
+(soft weights, dW), reconstruction loss and gradient (two bf16 MFMA
+products), relaxed backward with the fused Lion update. The workload is a
+Llama-3.1-8B-shaped q_proj: W 4096x4096 bf16 ~N(0, 0.02^2), 2-bit grid with
+four fp32 logits per weight, group-128 scales, 4096 calibration tokens of
+bf16 N(0,1) activations with 1 % outlier channels x20, Lion lr 1e-3.
+
+Prints one JSON line: weights/s over the timed steps, per-call times from HIP
+events recorded on the launch stream, the roofline of the dominant kernel,
+and the CPU oracle's rate on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+WORKLOAD = "qproj4096_int2"
+# Algorithmic bytes per weight coordinate per call (2-bit grid, L = 4 fp32
+# logits, bf16 W): forward reads 4 logits + W and writes dW (16 + 2 + 2);
+# backward reads G, 4 logits, 4 momenta and writes 4 logits, 4 momenta
+# (4 + 16 + 16 + 16 + 16). Group scale traffic (< 0.2 B) is left out.
+FWD_BYTES_PER_COORD = 20
+BWD_BYTES_PER_COORD = 68
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qproj4096_int2.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "post_weight_quantization_philox_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, launches_bytes: float):
+    """HBM bytes per launch from the committed counter runs, if they were
+    taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(data, rows: int):
+    """The oracle (NumPy fp64) on the first ``rows`` rows of the layer: one
+    full step (relaxed forward, both products against all 4096 tokens,
+    backward, Lion on logits and scales)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:            # threadpoolctl missing: report one thread
+        blas_threads = 1
+    W = data["W"][:rows]
+    X = data["X"]
+    scales, codes, logits = oracle.init_rtn(W, oracle.GRID_INT2)
+    state = {"logits": logits, "mom": np.zeros_like(logits), "scales": scales,
+             "scale_mom": np.zeros_like(scales), "codes": codes}
+    t0 = time.perf_counter()
+    oracle.step(state, W, X, oracle.GRID_INT2, 0, 1.0, 0, 0, 1e-3, 1e-5, bf16_dW=True)
+    dt = time.perf_counter() - t0
+    return {"value": rows * W.shape[1] / dt, "unit": "weights/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": f"one full step on rows 0..{rows - 1} of the 4096x4096 layer "
+                      f"({rows * W.shape[1]} weights) against all 4096 tokens, {dt:.1f} s; "
+                      f"NumPy elementwise work on one thread, BLAS on {blas_threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the step shards by output rows with no "
+              f"communication, so --gpus {args.gpus} is not run here", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synthetic
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver, tau_schedule
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    g.lib()
+    dev = torch.device("cuda:0")
+    data = synthetic.generate(WORKLOAD, seed=0)
+    wl = data["workload"]
+    Wd = torch.from_numpy(data["W_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    Xd = torch.from_numpy(data["X_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    solver = LayerSolver(Wd, Xd, g.GRID_INT2, seed=0, stream_id=0,
+                         lion=g.GsqLion.make(lr_logit=wl.lr_logit, lr_scale=1e-5))
+    M, K, N = solver.rows, solver.cols, solver.tokens
+    coords = M * K
+
+    # A plain copy of known size, untimed: its counter readings calibrate
+    # FETCH_SIZE / WRITE_SIZE in the profiler runs.
+    cal_src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+
+    taus = tau_schedule(args.warmup + args.steps)
+    for t in range(args.warmup):
+        solver.step(t, taus[t])
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        t = args.warmup + i
+        e = ev[i]
+        e[0].record(stream)
+        solver.relax_fwd(t, taus[t])
+        e[1].record(stream)
+        solver.recon()
+        e[2].record(stream)
+        solver.relax_bwd_lion(t, taus[t])
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    loss = float(solver.loss.item())
+
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    rec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    ms_per_step = elapsed * 1e3 / args.steps
+    gemm_flops = 4.0 * N * M * K
+    kernels = {
+        "relax_fwd": {"ms": fwd_ms, "GB/s": FWD_BYTES_PER_COORD * coords / fwd_ms / 1e6},
+        "recon_loss_grad": {"ms": rec_ms, "TFLOP/s": gemm_flops / rec_ms / 1e9,
+                            "note": "two bf16 GEMMs (2NMK flops each) + loss finalize"},
+        "relax_bwd_lion": {"ms": bwd_ms, "GB/s": BWD_BYTES_PER_COORD * coords / bwd_ms / 1e6},
+    }
+    # Dominant single kernel: the recon call is two GEMM launches (equal
+    # flops) plus a few-microsecond loss finalize, so each GEMM launch is
+    # weighed at half the call.
+    per_launch = {"relax_fwd": fwd_ms, "recon_loss_grad": rec_ms / 2, "relax_bwd_lion": bwd_ms}
+    dominant = max(per_launch, key=per_launch.get)
+    if dominant == "recon_loss_grad":
+        ach = kernels[dominant]["TFLOP/s"]
+        roof = {"bound": "mfma", "kernel": "gemm_nt_kernel (both launches of the call)",
+                "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
+    else:
+        per = FWD_BYTES_PER_COORD if dominant == "relax_fwd" else BWD_BYTES_PER_COORD
+        ach = kernels[dominant]["GB/s"]
+        roof = {"bound": "hbm", "kernel": dominant + "_kernel", "achieved": ach,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": measured_traffic(dominant, per * coords),
+                "algorithmic_bytes_per_launch": per * coords}
+
+    out = {
+        "metric": "GSQ relax step weights/sec (fwd+recon+bwd+Lion)",
+        "value": coords * args.steps / elapsed,
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 relax+Lion, bf16 MFMA (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "q_proj 4096x4096 bf16, 2-bit grid (4 fp32 logits/weight), "
+                               "group 128, 4096 tokens bf16 N(0,1) with 1% outlier channels x20",
+                   "rows": M, "cols": K, "tokens": N, "grid": "int2", "lion_lr": wl.lr_logit},
+        "roofline": roof,
+        "kernels": kernels,
+        "last_loss": loss,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(data, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

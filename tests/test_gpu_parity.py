@@ -19,11 +19,13 @@ pytestmark = pytest.mark.gpu
 GRIDS = [oracle.GRID_INT2, oracle.GRID_TERNARY, oracle.GRID_INT3_LOCAL]
 SHAPES = [(64, 512), (5, 384)]          # several scale groups per row; ragged row count
 
-# fp32 evaluation error of y = (l*log2e + eta*g*log2e)/tau, relative to the
-# natural scale of the soft weight (s * q_max) or of the gradient:
-# 1e-5 plus a term growing like (|l| + |g|) * 2^-22 / tau.
+# Soft weights and logit gradients: 1e-5 of their natural scale (s * q_max,
+# and |G| * s * q_max / tau). The fp32 evaluation of y = (l + eta*g)/tau can
+# in the worst case reach about 2^-22 * (|l| + |g|) / tau (4e-5 at tau = 0.05);
+# measured maxima on these inputs stay below 4e-6 at tau = 0.05, so the
+# tolerance is the flat 1e-5 for every tau >= 0.05.
 def z_tol(tau, lmax):
-    return 1e-5 + 2.0 ** -22 * (lmax + 18.0) / tau
+    return 1e-5
 
 
 @pytest.fixture(scope="module")
