@@ -17,6 +17,8 @@
 // (the dispatcher deals workgroups round-robin over the 8 XCDs) and tiles are
 // ordered in groups of 4 tile-rows, which keeps each XCD's A and B panels in
 // its own L2.
+#include <type_traits>
+
 #include "gsq_internal.hpp"
 
 namespace gsq {
@@ -64,10 +66,18 @@ __device__ __forceinline__ void tile_of(const GemmArgs& g, int& ti, int& tj) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// LDS swizzle: logical 16-byte chunk c of tile row r sits at physical chunk
+// c ^ ((r >> 1) & 7). A ds_read_b128 is served 16 lanes at a time across 64
+// four-byte banks (256 bytes); a 128-byte row covers half of them, so rows of
+// equal parity share banks. Fragment reads take 16 consecutive rows at one
+// logical chunk: the 8 even and the 8 odd rows each land on 8 distinct
+// physical chunks, which makes the access conflict-free.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
 // One K-step of one operand tile: 256 rows x 64 bf16 = 32 KiB, written by
 // direct global->LDS loads. Wave w, load q fills tile rows R0..R0+7 with
 // R0 = 8*(4q + w); lane l lands at LDS row R0 + l/8, physical chunk l%8, and
-// therefore fetches logical chunk (l%8) ^ (row & 7) of its row (the swizzle).
+// therefore fetches logical chunk (l%8) ^ swz(row) of its row.
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[8], uint32_t koff,
                                          uint4* tile, int wave) {
 #pragma unroll
@@ -79,6 +89,15 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const uint32
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier without a memory fence (the explicit waits give the
+// ordering); the empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void bar() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 template <int EPI>
 __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
@@ -102,11 +121,11 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
     const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(g.B), 0, g.b_bytes, 0x00020000);
     const int lrow = lane >> 3;
-    const int lch = (lane & 7) ^ (lrow & 7);
     uint32_t oa[8], ob[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int row = 8 * (4 * q + wave) + lrow;
+        const int lch = (lane & 7) ^ swz(row);
         const int rowa = i0 + row, rowb = j0 + row;
         oa[q] = rowa < g.I ? static_cast<uint32_t>((static_cast<int64_t>(rowa) * g.lda + lch * 8) * 2) : kOob;
         ob[q] = rowb < g.J ? static_cast<uint32_t>((static_cast<int64_t>(rowb) * g.ldb + lch * 8) * 2) : kOob;
@@ -121,39 +140,84 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
     // Fragment addressing: lane reads row (lane & 31) of a 32-row block, chunk
-    // 2*kk + (lane >> 5) of the 64-wide K slice; block rows are multiples of
-    // 8, so the swizzle term is (lane & 7).
+    // 2*kk + (lane >> 5) of the 64-wide K slice; block rows start at multiples
+    // of 32, so the swizzle term is swz(lane & 31).
     const int frow = lane & 31;
     const int fhalf = lane >> 5;
-    const int fsw = lane & 7;
+    const int fsw = swz(frow);
     const int rowA = wi * 128 + frow;
     const int rowB = wj * 128 + frow;
 
-    auto compute = [&](const uint4* tA, const uint4* tB) {
-        bf16x8 fa[2][4], fb[2][4];
-        auto fetch = [&](int kk, int slot) {
-            const int ch = (2 * kk + fhalf) ^ fsw;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                fa[slot][b] = __builtin_bit_cast(bf16x8, tA[(rowA + 32 * b) * kChunks + ch]);
-                fb[slot][b] = __builtin_bit_cast(bf16x8, tB[(rowB + 32 * b) * kChunks + ch]);
-            }
-        };
-        fetch(0, 0);
+    bf16x8 fa[2][4], fb[2][4];
+    auto read_a = [&](const uint4* t, int kk, int b) {
+        return __builtin_bit_cast(bf16x8, t[(rowA + 32 * b) * kChunks + ((2 * kk + fhalf) ^ fsw)]);
+    };
+    auto read_b = [&](const uint4* t, int kk, int b) {
+        return __builtin_bit_cast(bf16x8, t[(rowB + 32 * b) * kChunks + ((2 * kk + fhalf) ^ fsw)]);
+    };
+    // DMA load d (0..15) of the next K-step: A loads q = 0..7, then B.
+    auto dma1 = [&](int d, uint32_t koff, uint4* nA, uint4* nB) {
+        const int q = d & 7;
+        const int r0 = 8 * (4 * q + wave);
+        if (d < 8)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rs, (lds_void*)(nA + r0 * kChunks), 16,
+                                                     oa[q] + koff, 0, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rs, (lds_void*)(nB + r0 * kChunks), 16,
+                                                     ob[q] + koff, 0, 0, 0);
+    };
+
+    // Fragment reads of one slice, in the order the next slice consumes
+    // them: B blocks 0-1, B 2-3, A 0-1, A 2-3 (two per sub-group), so a
+    // block's MFMAs never wait on a read issued just before them.
+    auto fetch2 = [&](const uint4* tA, const uint4* tB, int kk, int slot, int part) {
+        if (part < 2) {
+            fb[slot][2 * part] = read_b(tB, kk, 2 * part);
+            fb[slot][2 * part + 1] = read_b(tB, kk, 2 * part + 1);
+        } else {
+            fa[slot][2 * part - 4] = read_a(tA, kk, 2 * part - 4);
+            fa[slot][2 * part - 3] = read_a(tA, kk, 2 * part - 3);
+        }
+    };
+
+    // One K-step, issued as 16 sub-groups (slice kk, A block a): two
+    // fragment reads for the next slice, two DMA loads of the next K-step
+    // (first two slices only, so they land before they are needed), and the
+    // 4 MFMAs of block a. The scheduling barriers keep this order, so memory
+    // instructions drain between MFMAs instead of blocking them in a burst.
+    // Halfway through the last slice the wave syncs with the others on the
+    // next buffer and fetches that buffer's first slice (B, then A), so the
+    // next step starts with its fragments in flight.
+    auto kstep = [&](auto has_next, const uint4* tA, const uint4* tB, uint4* nA, uint4* nB,
+                     uint32_t knext) {
+        constexpr bool kNext = decltype(has_next)::value;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            // The next slice's fragments are requested before this slice's 16
-            // MFMAs so the LDS latency hides behind them; the scheduling
-            // barriers keep the compiler from sinking the reads to their uses.
-            if (kk + 1 < 4) fetch(kk + 1, (kk + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
+            const int cur = kk & 1, nxt = cur ^ 1;
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 4; ++a) {
+                if constexpr (kNext) {
+                    if (kk < 2) {
+                        dma1(2 * (4 * kk + a), knext, nA, nB);
+                        dma1(2 * (4 * kk + a) + 1, knext, nA, nB);
+                    }
+                    if (kk == 3 && a == 2) {
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        wait_dma();
+                        bar();
+                    }
+                    if (kk == 3 && a >= 2) {
+                        fetch2(nA, nB, 0, 0, 2 * (a - 2));
+                        fetch2(nA, nB, 0, 0, 2 * (a - 2) + 1);
+                    }
+                }
+                if (kk < 3) fetch2(tA, tB, kk + 1, nxt, a);
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][a], fb[kk & 1][b],
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b],
                                                                         acc[a][b], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
@@ -162,17 +226,23 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
     dma_tile(ra_rs, oa, 0, sA0, wave);
     dma_tile(rb_rs, ob, 0, sB0, wave);
     wait_dma();
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool odd = kt & 1;
-        if (kt + 1 < nk) {
-            dma_tile(ra_rs, oa, (kt + 1) * kStep, odd ? sA0 : sA1, wave);
-            dma_tile(rb_rs, ob, (kt + 1) * kStep, odd ? sB0 : sB1, wave);
-        }
-        compute(odd ? sA1 : sA0, odd ? sB1 : sB0);
-        wait_dma();
-        __syncthreads();
+    bar();
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        fa[0][b] = read_a(sA0, 0, b);
+        fb[0][b] = read_b(sB0, 0, b);
     }
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+        const bool odd = kt & 1;
+        kstep(std::true_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1,
+              static_cast<uint32_t>(kt + 1) * kStep);
+    }
+    {
+        const bool odd = (nk - 1) & 1;
+        kstep(std::false_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0, nullptr, nullptr, 0u);
+    }
+    // All waves are done with the operand buffers before the epilogue reuses them.
+    __syncthreads();
 
     // Epilogue, one 32-row slab of the wave's 128x128 sub-tile at a time:
     // accumulators go to a private 32x128 fp32 LDS slab (register r of block
@@ -180,7 +250,10 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
     // lane reads back 8 consecutive values of one row and stores them as one
     // 16-byte (bf16) or two 16-byte (fp32) vectors. N and K are multiples of
     // 8, so a vector is entirely inside or outside the matrix.
-    float* slab = reinterpret_cast<float*>(wave < 2 ? sA0 : sB0) + (wave & 1) * (32 * 128);
+    constexpr int kSlab = 128 + 4;      // padded row: the two half-waves' rows
+                                        // start 16 bytes apart in the banks
+    // One 32 KiB buffer per wave.
+    float* slab = reinterpret_cast<float*>(wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1);
     const int grow0 = i0 + wi * 128;
     const int gcol0 = j0 + wj * 128;
     float lsum = 0.0f;
@@ -191,7 +264,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = 8 * (r >> 2) + 4 * fhalf + (r & 3);
-                slab[row * 128 + 32 * b + frow] = acc[a][b][r];
+                slab[row * kSlab + 32 * b + frow] = acc[a][b][r];
             }
         }
         __syncthreads();
@@ -199,8 +272,8 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
         for (int t = 0; t < 8; ++t) {
             const int c = lane + 64 * t;          // 512 chunks of 8 values
             const int row = c >> 4, col = (c & 15) * 8;
-            const float4 v0 = *reinterpret_cast<const float4*>(slab + row * 128 + col);
-            const float4 v1 = *reinterpret_cast<const float4*>(slab + row * 128 + col + 4);
+            const float4 v0 = *reinterpret_cast<const float4*>(slab + row * kSlab + col);
+            const float4 v1 = *reinterpret_cast<const float4*>(slab + row * kSlab + col + 4);
             const int grow = grow0 + a * 32 + row, gcol = gcol0 + col;
             if (grow < g.I && gcol < g.J) {
                 const int64_t off = static_cast<int64_t>(grow) * g.ldc + gcol;
