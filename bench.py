@@ -30,9 +30,11 @@ WORKLOAD = "qproj4096_int2"
 # Algorithmic bytes per weight coordinate per call (2-bit grid, L = 4 fp32
 # logits, bf16 W): forward reads 4 logits + W and writes dW (16 + 2 + 2);
 # backward reads G, 4 logits, 4 momenta and writes 4 logits, 4 momenta
-# (4 + 16 + 16 + 16 + 16). Group scale traffic (< 0.2 B) is left out.
+# (4 + 16 + 16 + 16 + 16); the fused backward + next forward adds W and dW
+# (68 + 2 + 2). Group scale traffic (< 0.2 B) is left out.
 FWD_BYTES_PER_COORD = 20
 BWD_BYTES_PER_COORD = 68
+FUSED_BYTES_PER_COORD = 72
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qproj4096_int2.json")
 
 
@@ -92,6 +94,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--unfused", action="store_true",
+                    help="time separate forward and backward calls instead of the fused pass")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the step shards by output rows with no "
@@ -124,43 +128,74 @@ def main():
     cal_dst = torch.empty_like(cal_src)
     cal_dst.copy_(cal_src)
 
-    taus = tau_schedule(args.warmup + args.steps)
-    for t in range(args.warmup):
-        solver.step(t, taus[t])
-    torch.cuda.synchronize()
-
+    taus = tau_schedule(args.warmup + args.steps + 1)
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        t = args.warmup + i
-        e = ev[i]
-        e[0].record(stream)
-        solver.relax_fwd(t, taus[t])
-        e[1].record(stream)
-        solver.recon()
-        e[2].record(stream)
-        solver.relax_bwd_lion(t, taus[t])
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    loss = float(solver.loss.item())
-
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    rec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    ms_per_step = elapsed * 1e3 / args.steps
     gemm_flops = 4.0 * N * M * K
-    kernels = {
-        "relax_fwd": {"ms": fwd_ms, "GB/s": FWD_BYTES_PER_COORD * coords / fwd_ms / 1e6},
-        "recon_loss_grad": {"ms": rec_ms, "TFLOP/s": gemm_flops / rec_ms / 1e9,
-                            "note": "two bf16 GEMMs (2NMK flops each) + loss finalize"},
-        "relax_bwd_lion": {"ms": bwd_ms, "GB/s": BWD_BYTES_PER_COORD * coords / bwd_ms / 1e6},
-    }
+    if args.unfused:
+        for t in range(args.warmup):
+            solver.step(t, taus[t])
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            t = args.warmup + i
+            e = ev[i]
+            e[0].record(stream)
+            solver.relax_fwd(t, taus[t])
+            e[1].record(stream)
+            solver.recon()
+            e[2].record(stream)
+            solver.relax_bwd_lion(t, taus[t])
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        rec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+        kernels = {
+            "relax_fwd": {"ms": fwd_ms, "GB/s": FWD_BYTES_PER_COORD * coords / fwd_ms / 1e6},
+            "recon_loss_grad": {"ms": rec_ms, "TFLOP/s": gemm_flops / rec_ms / 1e9,
+                                "note": "two bf16 GEMMs (2NMK flops each) + loss finalize"},
+            "relax_bwd_lion": {"ms": bwd_ms, "GB/s": BWD_BYTES_PER_COORD * coords / bwd_ms / 1e6},
+        }
+        per_launch = {"relax_fwd": fwd_ms, "recon_loss_grad": rec_ms / 2, "relax_bwd_lion": bwd_ms}
+        bytes_per = {"relax_fwd": FWD_BYTES_PER_COORD, "relax_bwd_lion": BWD_BYTES_PER_COORD}
+    else:
+        # Step t = objective of step t (dW from the previous pass) + backward
+        # and Lion of step t fused with the forward of step t + 1.
+        solver.relax_fwd(0, taus[0])
+        for t in range(args.warmup):
+            solver.step_fused(t, taus[t], taus[t + 1])
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            t = args.warmup + i
+            e = ev[i]
+            e[0].record(stream)
+            solver.recon()
+            e[1].record(stream)
+            solver.relax_bwd_lion_fwd(t, taus[t], t + 1, taus[t + 1])
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        rec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        fus_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        kernels = {
+            "recon_loss_grad": {"ms": rec_ms, "TFLOP/s": gemm_flops / rec_ms / 1e9,
+                                "note": "two bf16 GEMMs (2NMK flops each) + loss finalize"},
+            "relax_bwd_lion_fwd": {"ms": fus_ms,
+                                   "GB/s": FUSED_BYTES_PER_COORD * coords / fus_ms / 1e6,
+                                   "note": "backward + Lion of step t and forward of step t+1"},
+        }
+        per_launch = {"recon_loss_grad": rec_ms / 2, "relax_bwd_lion_fwd": fus_ms}
+        bytes_per = {"relax_bwd_lion_fwd": FUSED_BYTES_PER_COORD}
+    loss = float(solver.loss.item())
+    ms_per_step = elapsed * 1e3 / args.steps
+
     # Dominant single kernel: the recon call is two GEMM launches (equal
     # flops) plus a few-microsecond loss finalize, so each GEMM launch is
     # weighed at half the call.
-    per_launch = {"relax_fwd": fwd_ms, "recon_loss_grad": rec_ms / 2, "relax_bwd_lion": bwd_ms}
     dominant = max(per_launch, key=per_launch.get)
     if dominant == "recon_loss_grad":
         ach = kernels[dominant]["TFLOP/s"]
@@ -168,7 +203,7 @@ def main():
                 "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
     else:
-        per = FWD_BYTES_PER_COORD if dominant == "relax_fwd" else BWD_BYTES_PER_COORD
+        per = bytes_per[dominant]
         ach = kernels[dominant]["GB/s"]
         roof = {"bound": "hbm", "kernel": dominant + "_kernel", "achieved": ach,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,

@@ -18,6 +18,8 @@
  *   gsq_relax_bwd_lion   dLoss/dlogits, dLoss/dscales, Lion on both, in place
  * and, once after the last step,
  *   gsq_harden_pack      argmax codes, packed bit-stream, fp16 scales.
+ * gsq_relax_bwd_lion_fwd fuses a step's backward + Lion with the next step's
+ * forward (same results, one pass over the logits).
  *
  * Conventions for every call:
  *  - Pointers named as tensors are DEVICE pointers, allocated and owned by the
@@ -204,6 +206,21 @@ gsq_status gsq_relax_bwd_lion(const gsq_layer* layer, const float* G,
                               uint32_t step, float tau, float noise_scale,
                               const gsq_lion* lion, float* grad_logits_dbg,
                               float* grad_scales_dbg, void* stream);
+
+/* Backward + Lion of step `step` followed by the relaxed forward of step
+ * `next_step` (temperature `next_tau`) on the updated logits and scales, in
+ * one pass over the layer. The results equal gsq_relax_bwd_lion(step, tau)
+ * followed by gsq_relax_fwd(next_step, next_tau, w_soft_dbg = NULL) bit for
+ * bit; the logits are read once instead of twice per step. Arguments as in
+ * those two calls (no debug outputs); noise_scale applies to both steps.
+ *   W        [rows][cols] in layer->w_dtype
+ *   dW_bf16  out [rows][cols] bf16, the next step's W_soft - W */
+gsq_status gsq_relax_bwd_lion_fwd(const gsq_layer* layer, const float* G, float* logits,
+                                  float* mom, float* scales, float* scale_mom,
+                                  const uint8_t* init_codes, const void* W, uint32_t step,
+                                  float tau, float noise_scale, const gsq_lion* lion,
+                                  uint32_t next_step, float next_tau, uint16_t* dW_bf16,
+                                  void* stream);
 
 /* Collapse to hard codes after annealing (agihunt.info method paragraph) in
  * the symmetric group-128 format with 16-bit scales (takeaway paragraph;

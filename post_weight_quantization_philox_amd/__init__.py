@@ -18,7 +18,8 @@ __all__ = [
     "GsqError", "GsqLayer", "GsqLion", "lib", "exported_symbols",
     "gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
     "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
-    "gsq_transpose_tokens", "gsq_relax_bwd_lion", "gsq_harden_pack", "gsq_noise_dump",
+    "gsq_transpose_tokens", "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd", "gsq_harden_pack",
+    "gsq_noise_dump",
 ]
 
 GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL = 0, 1, 2
@@ -31,8 +32,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsq.so")
 #: Entry points declared in include/gsq.h.
 EXPORTS = ("gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
            "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
-           "gsq_transpose_tokens", "gsq_relax_bwd_lion", "gsq_harden_pack",
-           "gsq_noise_dump")
+           "gsq_transpose_tokens", "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd",
+           "gsq_harden_pack", "gsq_noise_dump")
 
 
 class GsqError(RuntimeError):
@@ -96,6 +97,9 @@ def lib() -> ctypes.CDLL:
         "gsq_transpose_tokens": (st, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
         "gsq_relax_bwd_lion": (st, [_L, _P, _P, _P, _P, _P, _P, ctypes.c_uint32, ctypes.c_float,
                                     ctypes.c_float, ctypes.POINTER(GsqLion), _P, _P, _P]),
+        "gsq_relax_bwd_lion_fwd": (st, [_L, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32,
+                                        ctypes.c_float, ctypes.c_float, ctypes.POINTER(GsqLion),
+                                        ctypes.c_uint32, ctypes.c_float, _P, _P]),
         "gsq_harden_pack": (st, [_L, _P, _P, _P, _P, _P, _P, _P]),
         "gsq_noise_dump": (st, [_L, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64, _P, _P]),
     }
@@ -206,6 +210,16 @@ def gsq_relax_bwd_lion(layer: GsqLayer, G, logits, mom, scales, scale_mom, init_
                                     _ptr(scales), _ptr(scale_mom), _ptr(init_codes), step, tau,
                                     noise_scale, ctypes.byref(lion), _ptr(grad_logits_dbg),
                                     _ptr(grad_scales_dbg), _stream(stream)))
+
+
+def gsq_relax_bwd_lion_fwd(layer: GsqLayer, G, logits, mom, scales, scale_mom, init_codes, W,
+                           step: int, tau: float, noise_scale: float, lion: GsqLion,
+                           next_step: int, next_tau: float, dW_bf16, stream=None):
+    _check("gsq_relax_bwd_lion_fwd",
+           lib().gsq_relax_bwd_lion_fwd(ctypes.byref(layer), _ptr(G), _ptr(logits), _ptr(mom),
+                                        _ptr(scales), _ptr(scale_mom), _ptr(init_codes), _ptr(W),
+                                        step, tau, noise_scale, ctypes.byref(lion), next_step,
+                                        next_tau, _ptr(dW_bf16), _stream(stream)))
 
 
 def gsq_harden_pack(layer: GsqLayer, logits, scales, init_codes, codes=None, packed=None,

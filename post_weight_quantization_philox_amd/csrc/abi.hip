@@ -219,7 +219,40 @@ gsq_status gsq_relax_bwd_lion(const gsq_layer* layer, const float* G, float* log
     GSQ_TRY(lion_consts(lion->lr_scale, lion, &lks));
     return hip_status(gsq::launch_relax_bwd_lion(d, G, logits, mom, scales, scale_mom, init_codes,
                                                  step, tk, lkl, lks, grad_logits_dbg,
-                                                 grad_scales_dbg, static_cast<hipStream_t>(stream)));
+                                                 grad_scales_dbg, nullptr, 0, tk, nullptr,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_relax_bwd_lion_fwd(const gsq_layer* layer, const float* G, float* logits,
+                                  float* mom, float* scales, float* scale_mom,
+                                  const uint8_t* init_codes, const void* W, uint32_t step,
+                                  float tau, float noise_scale, const gsq_lion* lion,
+                                  uint32_t next_step, float next_tau, uint16_t* dW_bf16,
+                                  void* stream) {
+    LayerDesc d;
+    GSQ_TRY(check_layer(layer, &d));
+    GSQ_TRY(need(G));
+    GSQ_TRY(need(logits));
+    GSQ_TRY(need(mom));
+    GSQ_TRY(need(scales));
+    GSQ_TRY(need(scale_mom));
+    GSQ_TRY(need(W));
+    GSQ_TRY(need(dW_bf16));
+    if (d.grid == GSQ_GRID_INT3_LOCAL) {
+        if (init_codes == nullptr) return GSQ_ERR_GRID;
+        GSQ_TRY(need(init_codes));
+    }
+    if (lion == nullptr) return GSQ_ERR_NULL;
+    gsq::TauK tk, tk_next;
+    GSQ_TRY(check_tau(tau, noise_scale, &tk));
+    GSQ_TRY(check_tau(next_tau, noise_scale, &tk_next));
+    gsq::LionK lkl, lks;
+    GSQ_TRY(lion_consts(lion->lr_logit, lion, &lkl));
+    GSQ_TRY(lion_consts(lion->lr_scale, lion, &lks));
+    return hip_status(gsq::launch_relax_bwd_lion(d, G, logits, mom, scales, scale_mom, init_codes,
+                                                 step, tk, lkl, lks, nullptr, nullptr, W,
+                                                 next_step, tk_next, dW_bf16,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 gsq_status gsq_harden_pack(const gsq_layer* layer, const float* logits, const float* scales,

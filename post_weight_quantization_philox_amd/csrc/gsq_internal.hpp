@@ -28,10 +28,13 @@ hipError_t launch_init_rtn(const LayerDesc& d, const void* W, float* scales, uin
 hipError_t launch_relax_fwd(const LayerDesc& d, const float* logits, const float* scales,
                             const uint8_t* codes, const void* W, uint32_t step, TauK tk,
                             uint16_t* dW, float* w_soft_dbg, hipStream_t st);
+// Backward + Lion; with dW != nullptr also the next step's forward (no
+// debug outputs in that mode).
 hipError_t launch_relax_bwd_lion(const LayerDesc& d, const float* G, float* logits, float* mom,
                                  float* scales, float* scale_mom, const uint8_t* codes,
                                  uint32_t step, TauK tk, LionK lk_logit, LionK lk_scale,
-                                 float* grad_logits_dbg, float* grad_scales_dbg, hipStream_t st);
+                                 float* grad_logits_dbg, float* grad_scales_dbg, const void* W,
+                                 uint32_t next_step, TauK tk_next, uint16_t* dW, hipStream_t st);
 hipError_t launch_harden_pack(const LayerDesc& d, const float* logits, const float* scales,
                               const uint8_t* codes, uint8_t* codes_out, uint32_t* packed,
                               uint16_t* scales_f16, hipStream_t st);

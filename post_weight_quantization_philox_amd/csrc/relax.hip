@@ -140,14 +140,18 @@ __global__ __launch_bounds__(kThreads) void relax_fwd_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Backward + Lion, in place. G = dLoss/dW_soft.
+// Backward + Lion, in place. G = dLoss/dW_soft. With FWD_NEXT the kernel then
+// runs the relaxed forward of the next step on the updated logits and scale
+// (still in registers): this equals a separate forward call, but the logits
+// are read from HBM once per step instead of twice.
 // ---------------------------------------------------------------------------
-template <int GRID, bool DBG>
+template <int GRID, bool DBG, bool FWD_NEXT, bool WBF16>
 __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
     const float* __restrict__ G, float* __restrict__ logits, float* __restrict__ mom,
     float* __restrict__ scales, float* __restrict__ scale_mom, const uint8_t* __restrict__ codes,
     uint64_t mk, uint32_t step, uint32_t sid, Key key, TauK tk, LionK lkl, LionK lks,
-    float* __restrict__ gl_dbg, float* __restrict__ gs_dbg) {
+    float* __restrict__ gl_dbg, float* __restrict__ gs_dbg, const void* __restrict__ W,
+    uint32_t next_step, TauK tk_next, uint16_t* __restrict__ dW) {
     constexpr int L = GridT<GRID>::L;
     const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
     // Whole scale groups (32 threads) are either in range or not, so the
@@ -161,46 +165,70 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
         load4(logits + k * mk + i0, l[k]);
         load4(mom + k * mk + i0, m[k]);
     }
+    float w[4];
+    if constexpr (FWD_NEXT) load_w4(W, WBF16, i0, w);
     const uint64_t grp = i0 >> 7;
     const float s = scales[grp];
     uint32_t cw = 0;
     if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = *reinterpret_cast<const uint32_t*>(codes + i0);
-    uint32_t nz[4 * L];
-    noise_words4<L>(i0, step, sid, key, nz);
     float gsum = 0.0f;
-    float gl[L][4];
+    {
+        uint32_t nz[4 * L];
+        noise_words4<L>(i0, step, sid, key, nz);
+        float gl[L][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        float lc[L];
+        for (int c = 0; c < 4; ++c) {
+            float lc[L];
 #pragma unroll
-        for (int k = 0; k < L; ++k) lc[k] = l[k][c];
-        Relaxed<GRID> r;
-        relax_coord<GRID>(lc, &nz[c * L], static_cast<int>((cw >> (8 * c)) & 0xFF), tk, r);
-        const float gsc = g[c] * s * tk.invtau;
-        if constexpr (GRID == GSQ_GRID_TERNARY) {
-            gl[0][c] = gsc * (r.a * r.abar) * r.sg;
-            gl[1][c] = gsc * (2.0f * r.a) * r.bb;
-        } else {
+            for (int k = 0; k < L; ++k) lc[k] = l[k][c];
+            Relaxed<GRID> r;
+            relax_coord<GRID>(lc, &nz[c * L], static_cast<int>((cw >> (8 * c)) & 0xFF), tk, r);
+            const float gsc = g[c] * s * tk.invtau;
+            if constexpr (GRID == GSQ_GRID_TERNARY) {
+                gl[0][c] = gsc * (r.a * r.abar) * r.sg;
+                gl[1][c] = gsc * (2.0f * r.a) * r.bb;
+            } else {
 #pragma unroll
-            for (int k = 0; k < L; ++k) gl[k][c] = gsc * r.p[k] * (r.v[k] - r.what);
+                for (int k = 0; k < L; ++k) gl[k][c] = gsc * r.p[k] * (r.v[k] - r.what);
+            }
+            gsum = __builtin_fmaf(g[c], r.what, gsum);
         }
-        gsum = __builtin_fmaf(g[c], r.what, gsum);
-    }
 #pragma unroll
-    for (int k = 0; k < L; ++k) {
+        for (int k = 0; k < L; ++k) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) lion_update(l[k][c], m[k][c], gl[k][c], lkl);
-        store4(logits + k * mk + i0, l[k]);
-        store4(mom + k * mk + i0, m[k]);
-        if constexpr (DBG) store4(gl_dbg + k * mk + i0, gl[k]);
+            for (int c = 0; c < 4; ++c) lion_update(l[k][c], m[k][c], gl[k][c], lkl);
+            store4(logits + k * mk + i0, l[k]);
+            store4(mom + k * mk + i0, m[k]);
+            if constexpr (DBG) store4(gl_dbg + k * mk + i0, gl[k]);
+        }
     }
-    gsum = group32_sum(gsum);
+    // Group sum, taken from the group's first lane so that every lane applies
+    // the same Lion update to the shared scale.
+    gsum = __shfl(group32_sum(gsum), threadIdx.x & 32, 64);
+    float sn = s, smn = scale_mom[grp];
+    lion_update(sn, smn, gsum, lks);
     if ((threadIdx.x & 31) == 0) {
-        float sn = s, smn = scale_mom[grp];
-        lion_update(sn, smn, gsum, lks);
         scales[grp] = sn;
         scale_mom[grp] = smn;
         if constexpr (DBG) gs_dbg[grp] = gsum;
+    }
+    if constexpr (FWD_NEXT) {
+        uint32_t nz[4 * L];
+        noise_words4<L>(i0, next_step, sid, key, nz);
+        float out[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float lc[L];
+#pragma unroll
+            for (int k = 0; k < L; ++k) lc[k] = l[k][c];
+            Relaxed<GRID> r;
+            relax_coord<GRID>(lc, &nz[c * L], static_cast<int>((cw >> (8 * c)) & 0xFF), tk_next, r);
+            out[c] = sn * r.what;
+        }
+        uint2 o;
+        o.x = pack_bf16x2(out[0] - w[0], out[1] - w[1]);
+        o.y = pack_bf16x2(out[2] - w[2], out[3] - w[3]);
+        *reinterpret_cast<uint2*>(dW + i0) = o;
     }
 }
 
@@ -383,12 +411,17 @@ hipError_t launch_relax_fwd(const LayerDesc& d, const float* logits, const float
 hipError_t launch_relax_bwd_lion(const LayerDesc& d, const float* G, float* logits, float* mom,
                                  float* scales, float* scale_mom, const uint8_t* codes,
                                  uint32_t step, TauK tk, LionK lkl, LionK lks,
-                                 float* gl_dbg, float* gs_dbg, hipStream_t st) {
+                                 float* gl_dbg, float* gs_dbg, const void* W, uint32_t next_step,
+                                 TauK tk_next, uint16_t* dW, hipStream_t st) {
     const unsigned nb = blocks_for(d.mk / 4);
     const bool dbg = gl_dbg != nullptr || gs_dbg != nullptr;
-#define GSQ_BWD(G_, DB) \
-    GSQ_LAUNCH((relax_bwd_lion_kernel<G_, DB>), nb, st, G, logits, mom, scales, scale_mom, codes, d.mk, step, d.sid, d.key, tk, lkl, lks, gl_dbg, gs_dbg)
-#define GSQ_BWD_G(G_) if (dbg) GSQ_BWD(G_, true); else GSQ_BWD(G_, false);
+    const bool fwd = dW != nullptr;
+#define GSQ_BWD(G_, DB, FW, WB) \
+    GSQ_LAUNCH((relax_bwd_lion_kernel<G_, DB, FW, WB>), nb, st, G, logits, mom, scales, scale_mom, codes, d.mk, step, d.sid, d.key, tk, lkl, lks, gl_dbg, gs_dbg, W, next_step, tk_next, dW)
+#define GSQ_BWD_G(G_)                                                   \
+    if (!fwd) { if (dbg) GSQ_BWD(G_, true, false, true); else GSQ_BWD(G_, false, false, true); } \
+    else if (d.w_bf16) GSQ_BWD(G_, false, true, true);                  \
+    else GSQ_BWD(G_, false, true, false);
     switch (d.grid) {
         case GSQ_GRID_INT2: GSQ_BWD_G(GSQ_GRID_INT2); break;
         case GSQ_GRID_TERNARY: GSQ_BWD_G(GSQ_GRID_TERNARY); break;

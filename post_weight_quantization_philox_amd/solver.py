@@ -24,7 +24,7 @@ import torch
 from . import (GRID_INT3_LOCAL, DTYPE_BF16, DTYPE_F32, N_LOGITS, CODE_BITS, GsqLayer,
                GsqLion, gsq_init_rtn, gsq_relax_fwd, gsq_recon_workspace_bytes,
                gsq_recon_loss_grad, gsq_transpose_tokens, gsq_relax_bwd_lion,
-               gsq_harden_pack)
+               gsq_relax_bwd_lion_fwd, gsq_harden_pack)
 
 TOKEN_ALIGN = 64
 
@@ -117,11 +117,28 @@ class LayerSolver:
                            self.init_codes, step, tau, noise_scale, self.lion, grad_logits_dbg,
                            grad_scales_dbg)
 
+    def relax_bwd_lion_fwd(self, step: int, tau: float, next_step: int, next_tau: float,
+                           noise_scale: float = 1.0):
+        gsq_relax_bwd_lion_fwd(self.layer, self.G, self.logits, self.mom, self.scales,
+                               self.scale_mom, self.init_codes, self.W, step, tau, noise_scale,
+                               self.lion, next_step, next_tau, self.dW)
+
     def step(self, step: int, tau: float, noise_scale: float = 1.0):
         """One relaxed-quantization step: forward, objective, backward + Lion."""
         self.relax_fwd(step, tau, noise_scale)
         self.recon()
         self.relax_bwd_lion(step, tau, noise_scale)
+
+    def step_fused(self, step: int, tau: float, next_tau: float | None,
+                   noise_scale: float = 1.0):
+        """Objective and backward + Lion of ``step`` (whose dW the previous
+        call, or :meth:`relax_fwd`, produced), fused with the forward of
+        ``step + 1`` at ``next_tau`` (None on the last step)."""
+        self.recon()
+        if next_tau is None:
+            self.relax_bwd_lion(step, tau, noise_scale)
+        else:
+            self.relax_bwd_lion_fwd(step, tau, step + 1, next_tau, noise_scale)
 
     def harden(self):
         """Hard codes (uint8), packed codes (int32 words) and fp16 scales."""
@@ -138,8 +155,10 @@ class LayerSolver:
         """The annealed solve; returns the per-step losses (host, every step
         if ``log_every`` is 1, else only those logged) and the hard result."""
         losses = []
-        for t, tau in enumerate(tau_schedule(steps, tau0, tau1)):
-            self.step(t, tau, noise_scale)
+        taus = tau_schedule(steps, tau0, tau1)
+        self.relax_fwd(0, taus[0], noise_scale)
+        for t, tau in enumerate(taus):
+            self.step_fused(t, tau, taus[t + 1] if t + 1 < steps else None, noise_scale)
             if log_every and (t % log_every == 0 or t == steps - 1):
                 losses.append(float(self.loss.item()))
         return losses, self.harden()

@@ -309,3 +309,39 @@ def test_harden_pack_bit_exact(dev, grid):
     np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
     np.testing.assert_array_equal(packed.cpu().numpy().view(np.uint32), p_ref)
     np.testing.assert_array_equal(s16.cpu().numpy().view(np.uint16), s_ref)
+
+
+# ----------------------------------------------------------------------------
+# Fused backward + Lion + next forward
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("w_bf16", [True, False])
+def test_fused_bwd_fwd_equals_separate_calls(dev, grid, w_bf16):
+    import torch
+    import post_weight_quantization_philox_amd as g
+    M, K = 40, 384
+    d, W, s, c0, lg = _layer_inputs(grid, M, K, seed=31, w_bf16=w_bf16)
+    rng = np.random.default_rng(8)
+    L = oracle.N_LOGITS[grid]
+    G = (rng.normal(0, 1.0, (M, K)) * 50.0).astype(np.float32)
+    mom = (rng.normal(0, 1.0, (L, M, K)) * 1e-2).astype(np.float32)
+    smom = (rng.normal(0, 1.0, s.shape) * 1e-3).astype(np.float32)
+    lion = g.GsqLion.make(lr_logit=3e-3, lr_scale=1e-4)
+    layer = g.GsqLayer.make(grid, M, K, g.DTYPE_BF16 if w_bf16 else g.DTYPE_F32, seed=3, stream=4)
+    Wd = _w_dev(d, dev)
+    codes = torch.from_numpy(c0).to(dev)
+    outs = []
+    for fused in (False, True):
+        t = [torch.from_numpy(x).to(dev) for x in (lg, mom, s, smom)]
+        dW = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        Gd = torch.from_numpy(G).to(dev)
+        if fused:
+            g.gsq_relax_bwd_lion_fwd(layer, Gd, *t, codes, Wd, 41, 0.37, 1.0, lion, 42, 0.31, dW)
+        else:
+            g.gsq_relax_bwd_lion(layer, Gd, *t, codes, 41, 0.37, 1.0, lion)
+            g.gsq_relax_fwd(layer, t[0], t[2], codes, Wd, 42, 0.31, 1.0, dW)
+        torch.cuda.synchronize()
+        outs.append([x.cpu().numpy() for x in t] + [dW.view(torch.int16).cpu().numpy()])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
