@@ -71,7 +71,7 @@ gsq_status lion_consts(float lr, const gsq_lion* l, gsq::LionK* k) {
     k->omb1 = 1.0f - l->beta1;
     k->b2 = l->beta2;
     k->omb2 = 1.0f - l->beta2;
-    k->wd = l->weight_decay;
+    k->nlrwd = -(lr * l->weight_decay);
     return GSQ_OK;
 }
 

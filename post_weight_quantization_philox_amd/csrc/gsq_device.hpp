@@ -11,7 +11,7 @@ namespace gsq {
 // published round function: the products M0*c0 and M1*c2 (32x32 -> 64 bit),
 // new counter (hi1^c1^k0, lo1, hi0^c3^k1, lo0), key bumped by the Weyl
 // constants between rounds. The key is wave-uniform, so its schedule stays in
-// scalar registers; each round costs two v_mad_u64_u32 and two xor3.
+// scalar registers; each round costs two v_mad_u64_u32 and two three-input xors.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
 constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
@@ -19,6 +19,12 @@ constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
 constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
 
 struct Key { uint32_t k0, k1; };
+
+// a ^ b ^ c in one VALU instruction: gfx950's three-input bitwise op with
+// truth table 0x96 (the compiler emits two v_xor_b32 for the plain expression).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
 
 __device__ __forceinline__ void philox_block(uint64_t blk, uint32_t step, uint32_t sid,
                                              Key key, uint32_t out[4]) {
@@ -31,8 +37,8 @@ __device__ __forceinline__ void philox_block(uint64_t blk, uint32_t step, uint32
     for (int r = 0; r < 10; ++r) {
         const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c0;
         const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c2;
-        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3(static_cast<uint32_t>(p1 >> 32), c1, k0);
+        const uint32_t n2 = xor3(static_cast<uint32_t>(p0 >> 32), c3, k1);
         c1 = static_cast<uint32_t>(p1);
         c3 = static_cast<uint32_t>(p0);
         c0 = n0;
@@ -53,6 +59,41 @@ __device__ __forceinline__ void noise_words4(uint64_t i0, uint32_t step, uint32_
 #pragma unroll
     for (int j = 0; j < L; ++j) philox_block(b0 + j, step, sid, key, &w[4 * j]);
 }
+
+// Lazy form of noise_words4: coordinate C (0..3) of the four starting at i0
+// takes words C*L .. C*L + L - 1 of the same block sequence. Blocks are
+// generated on demand, in order, with at most two live (the last two), so the
+// words of all four coordinates never occupy registers at once. Which blocks
+// are new for coordinate C is known at compile time.
+template <int L>
+struct NoiseStream4 {
+    uint64_t b0;
+    uint32_t step, sid;
+    Key key;
+    uint32_t cur[4], nxt[4];   // after words<C>(): blocks hi(C) - 1 and hi(C)
+
+    __device__ __forceinline__ NoiseStream4(uint64_t i0, uint32_t step_, uint32_t sid_, Key key_)
+        : b0((i0 >> 2) * L), step(step_), sid(sid_), key(key_) {}
+
+    // Calls must come in order C = 0, 1, 2, 3.
+    template <int C>
+    __device__ __forceinline__ void words(uint32_t (&w)[L]) {
+        constexpr int first = C * L;
+        constexpr int hi = (first + L - 1) / 4;          // last block this coordinate uses
+        constexpr int done = C == 0 ? -1 : (first - 1) / 4;   // last block generated before
+#pragma unroll
+        for (int b = done + 1; b <= hi; ++b) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+            philox_block(b0 + b, step, sid, key, nxt);
+        }
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const int word = first + j;
+            w[j] = (word / 4 == hi) ? nxt[word & 3] : cur[word & 3];
+        }
+    }
+};
 
 // Uniform in (0,1): top 24 bits forced odd, times 2^-24 (exact in fp32).
 __device__ __forceinline__ float uniform24(uint32_t x) {
@@ -122,16 +163,21 @@ __device__ __forceinline__ float group32_max(float v) {
 }
 
 // Lion on one fp32 parameter (Chen et al. 2023). The sign is taken on
-// c = fma(beta1, m, fp32((1-beta1)*g)); theta -= lr*(sign(c) + wd*theta);
+// c = fma(beta1, m, fp32((1-beta1)*g)); theta <- theta - lr*sign(c) - lr*wd*theta;
 // m = fma(beta2, m, fp32((1-beta2)*g)).
 struct LionK {
-    float lr, b1, omb1, b2, omb2, wd;
+    float lr, b1, omb1, b2, omb2, nlrwd;   // nlrwd = -lr * wd (fp32)
 };
 
+// theta - lr*sign(c) is formed as theta - copysign(lr, c) (v_bfi_b32 on the
+// sign bit), zero when c == 0; the decay term is then one fma with
+// -lr*wd, which leaves the value unchanged when wd = 0.
 __device__ __forceinline__ void lion_update(float& theta, float& m, float g, const LionK& k) {
     const float c = __builtin_fmaf(k.b1, m, __fmul_rn(k.omb1, g));
-    const float sgn = (c > 0.0f) ? 1.0f : ((c < 0.0f) ? -1.0f : 0.0f);
-    theta = __builtin_fmaf(-k.lr, __builtin_fmaf(k.wd, theta, sgn), theta);
+    const float step = __uint_as_float((__float_as_uint(k.lr) & 0x7FFFFFFFu) |
+                                       (__float_as_uint(c) & 0x80000000u));
+    const float moved = __fsub_rn(theta, c != 0.0f ? step : 0.0f);
+    theta = __builtin_fmaf(k.nlrwd, theta, moved);
     m = __builtin_fmaf(k.b2, m, __fmul_rn(k.omb2, g));
 }
 

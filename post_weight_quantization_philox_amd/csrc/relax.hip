@@ -8,6 +8,8 @@
 // coordinates; the two halves of a wave are two groups, reduced with lane
 // shuffles. The four coordinates' noise is a whole number of Philox blocks
 // (L blocks for L logits), so no word is generated twice.
+#include <type_traits>
+
 #include "gsq_internal.hpp"
 
 namespace gsq {
@@ -21,12 +23,33 @@ template <> struct GridT<GSQ_GRID_INT2> { static constexpr int L = 4; static con
 template <> struct GridT<GSQ_GRID_TERNARY> { static constexpr int L = 2; static constexpr int QMAX = 1; static constexpr int BITS = 2; };
 template <> struct GridT<GSQ_GRID_INT3_LOCAL> { static constexpr int L = 5; static constexpr int QMAX = 7; static constexpr int BITS = 3; };
 
-__device__ __forceinline__ void load_w4(const void* W, bool bf16, uint64_t i0, float w[4]) {
+// Element i of a tensor whose planes start at wave-uniform bases. With O32
+// the byte offset of i fits 32 bits (checked by the launcher: rows*cols*4 <
+// 2^32), so every access is a uniform 64-bit base plus one 32-bit per-thread
+// offset (the global saddr form): one offset register serves every plane.
+template <bool O32>
+struct Idx {
+    uint64_t i;
+    template <typename T>
+    __device__ __forceinline__ T* at(T* base, uint64_t plane_elems = 0, int plane = 0) const {
+        T* b = base + plane_elems * plane;
+        if constexpr (O32) {
+            const uint32_t off = static_cast<uint32_t>(i) * static_cast<uint32_t>(sizeof(T));
+            using C = typename std::conditional<std::is_const<T>::value, const char, char>::type;
+            return reinterpret_cast<T*>(reinterpret_cast<C*>(b) + off);
+        } else {
+            return b + i;
+        }
+    }
+};
+
+template <bool O32>
+__device__ __forceinline__ void load_w4(const void* W, bool bf16, Idx<O32> ix, float w[4]) {
     if (bf16) {
-        const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(W) + i0);
+        const uint2 v = *reinterpret_cast<const uint2*>(ix.at(static_cast<const uint16_t*>(W)));
         w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x); w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
     } else {
-        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + i0);
+        const float4 v = *reinterpret_cast<const float4*>(ix.at(static_cast<const float*>(W)));
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     }
 }
@@ -38,6 +61,14 @@ __device__ __forceinline__ void load4(const float* p, float v[4]) {
 
 __device__ __forceinline__ void store4(float* p, const float v[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <int C> using Ci = std::integral_constant<int, C>;
+
+// Calls f(Ci<0>{}) .. f(Ci<3>{}) in order.
+template <typename F>
+__device__ __forceinline__ void for4(F&& f) {
+    f(Ci<0>{}); f(Ci<1>{}); f(Ci<2>{}); f(Ci<3>{});
 }
 
 // Candidate value (scale units) of local-shift logit k around code c0:
@@ -52,7 +83,8 @@ __device__ __forceinline__ float local_value(int c0, int k) {
 template <int GRID>
 struct Relaxed {
     static constexpr int L = GridT<GRID>::L;
-    float p[L];   // softmax probabilities (2-bit, local shift)
+    float e[L];   // unnormalised softmax weights 2^(y_k - y_max) (2-bit, local shift)
+    float inv;    // 1 / sum_k e_k, so p_k = e_k * inv
     float v[L];   // candidate values in scale units
     float what;   // soft weight in scale units
     // ternary pieces: a = P(mask on), abar = 1 - a, sg = 2b - 1, bb = b(1-b)
@@ -90,21 +122,19 @@ __device__ __forceinline__ void relax_coord(const float (&l)[GridT<GRID>::L], co
 #pragma unroll
         for (int k = 0; k < L; ++k) {
             r.v[k] = (GRID == GSQ_GRID_INT2) ? static_cast<float>(2 * k - 3) : local_value(c0, k);
-            r.p[k] = hw_exp2(y[k] - ymax);
-            sum += r.p[k];
-            num = __builtin_fmaf(r.p[k], r.v[k], num);
+            r.e[k] = hw_exp2(y[k] - ymax);
+            sum += r.e[k];
+            num = __builtin_fmaf(r.e[k], r.v[k], num);
         }
-        const float inv = hw_rcp(sum);
-#pragma unroll
-        for (int k = 0; k < L; ++k) r.p[k] *= inv;
-        r.what = num * inv;
+        r.inv = hw_rcp(sum);
+        r.what = num * r.inv;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Forward: dW = s*w_hat - W, bf16.
 // ---------------------------------------------------------------------------
-template <int GRID, bool WBF16, bool DBG>
+template <int GRID, bool WBF16, bool DBG, bool O32>
 __global__ __launch_bounds__(kThreads) void relax_fwd_kernel(
     const float* __restrict__ logits, const float* __restrict__ scales,
     const uint8_t* __restrict__ codes, const void* __restrict__ W, uint64_t mk, uint32_t step,
@@ -112,31 +142,33 @@ __global__ __launch_bounds__(kThreads) void relax_fwd_kernel(
     constexpr int L = GridT<GRID>::L;
     const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
     if (i0 >= mk) return;
+    const Idx<O32> ix{i0};
     float l[L][4];
 #pragma unroll
-    for (int k = 0; k < L; ++k) load4(logits + k * mk + i0, l[k]);
+    for (int k = 0; k < L; ++k) load4(ix.at(logits, mk, k), l[k]);
     float w[4];
-    load_w4(W, WBF16, i0, w);
+    load_w4(W, WBF16, ix, w);
     const float s = scales[i0 >> 7];
     uint32_t cw = 0;
-    if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = *reinterpret_cast<const uint32_t*>(codes + i0);
-    uint32_t nz[4 * L];
-    noise_words4<L>(i0, step, sid, key, nz);
+    if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = *reinterpret_cast<const uint32_t*>(ix.at(codes));
+    NoiseStream4<L> ns(i0, step, sid, key);
     float out[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for4([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        uint32_t nz[L];
+        ns.template words<c>(nz);
         float lc[L];
 #pragma unroll
         for (int k = 0; k < L; ++k) lc[k] = l[k][c];
         Relaxed<GRID> r;
-        relax_coord<GRID>(lc, &nz[c * L], static_cast<int>((cw >> (8 * c)) & 0xFF), tk, r);
+        relax_coord<GRID>(lc, nz, static_cast<int>((cw >> (8 * c)) & 0xFF), tk, r);
         out[c] = s * r.what;
-    }
-    if constexpr (DBG) store4(w_soft_dbg + i0, out);
+    });
+    if constexpr (DBG) store4(ix.at(w_soft_dbg), out);
     uint2 o;
     o.x = pack_bf16x2(out[0] - w[0], out[1] - w[1]);
     o.y = pack_bf16x2(out[2] - w[2], out[3] - w[3]);
-    *reinterpret_cast<uint2*>(dW + i0) = o;
+    *reinterpret_cast<uint2*>(ix.at(dW)) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -145,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void relax_fwd_kernel(
 // (still in registers): this equals a separate forward call, but the logits
 // are read from HBM once per step instead of twice.
 // ---------------------------------------------------------------------------
-template <int GRID, bool DBG, bool FWD_NEXT, bool WBF16>
+template <int GRID, bool DBG, bool FWD_NEXT, bool WBF16, bool O32>
 __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
     const float* __restrict__ G, float* __restrict__ logits, float* __restrict__ mom,
     float* __restrict__ scales, float* __restrict__ scale_mom, const uint8_t* __restrict__ codes,
@@ -157,49 +189,56 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
     // Whole scale groups (32 threads) are either in range or not, so the
     // shuffles below never read a lane that returned here.
     if (i0 >= mk) return;
+    const Idx<O32> ix{i0};
     float g[4];
-    load4(G + i0, g);
+    load4(ix.at(G), g);
     float l[L][4], m[L][4];
 #pragma unroll
     for (int k = 0; k < L; ++k) {
-        load4(logits + k * mk + i0, l[k]);
-        load4(mom + k * mk + i0, m[k]);
+        load4(ix.at(logits, mk, k), l[k]);
+        load4(ix.at(mom, mk, k), m[k]);
     }
-    float w[4];
-    if constexpr (FWD_NEXT) load_w4(W, WBF16, i0, w);
     const uint64_t grp = i0 >> 7;
     const float s = scales[grp];
     uint32_t cw = 0;
-    if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = *reinterpret_cast<const uint32_t*>(codes + i0);
+    if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = *reinterpret_cast<const uint32_t*>(ix.at(codes));
     float gsum = 0.0f;
     {
-        uint32_t nz[4 * L];
-        noise_words4<L>(i0, step, sid, key, nz);
-        float gl[L][4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        NoiseStream4<L> ns(i0, step, sid, key);
+        const float gs_tau = s * tk.invtau;
+        // Each coordinate's gradient goes straight into its Lion update, so
+        // no gradient array stays live (fewer registers, more waves in flight).
+        for4([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            uint32_t nz[L];
+            ns.template words<c>(nz);
             float lc[L];
 #pragma unroll
             for (int k = 0; k < L; ++k) lc[k] = l[k][c];
             Relaxed<GRID> r;
-            relax_coord<GRID>(lc, &nz[c * L], static_cast<int>((cw >> (8 * c)) & 0xFF), tk, r);
-            const float gsc = g[c] * s * tk.invtau;
+            relax_coord<GRID>(lc, nz, static_cast<int>((cw >> (8 * c)) & 0xFF), tk, r);
+            const float gsc = g[c] * gs_tau;
+            float glc[L];
             if constexpr (GRID == GSQ_GRID_TERNARY) {
-                gl[0][c] = gsc * (r.a * r.abar) * r.sg;
-                gl[1][c] = gsc * (2.0f * r.a) * r.bb;
+                glc[0] = gsc * (r.a * r.abar) * r.sg;
+                glc[1] = gsc * (2.0f * r.a) * r.bb;
             } else {
+                // p_k = e_k / sum: the normalisation rides on the common factor.
+                const float gn = gsc * r.inv;
 #pragma unroll
-                for (int k = 0; k < L; ++k) gl[k][c] = gsc * r.p[k] * (r.v[k] - r.what);
+                for (int k = 0; k < L; ++k) glc[k] = gn * r.e[k] * (r.v[k] - r.what);
             }
             gsum = __builtin_fmaf(g[c], r.what, gsum);
-        }
+#pragma unroll
+            for (int k = 0; k < L; ++k) {
+                if constexpr (DBG) ix.at(gl_dbg, mk, k)[c] = glc[k];
+                lion_update(l[k][c], m[k][c], glc[k], lkl);
+            }
+        });
 #pragma unroll
         for (int k = 0; k < L; ++k) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) lion_update(l[k][c], m[k][c], gl[k][c], lkl);
-            store4(logits + k * mk + i0, l[k]);
-            store4(mom + k * mk + i0, m[k]);
-            if constexpr (DBG) store4(gl_dbg + k * mk + i0, gl[k]);
+            store4(ix.at(logits, mk, k), l[k]);
+            store4(ix.at(mom, mk, k), m[k]);
         }
     }
     // Group sum, taken from the group's first lane so that every lane applies
@@ -213,22 +252,26 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
         if constexpr (DBG) gs_dbg[grp] = gsum;
     }
     if constexpr (FWD_NEXT) {
-        uint32_t nz[4 * L];
-        noise_words4<L>(i0, next_step, sid, key, nz);
+        // W is only needed here; its load overlaps the next-step noise.
+        float w[4];
+        load_w4(W, WBF16, ix, w);
+        NoiseStream4<L> ns(i0, next_step, sid, key);
         float out[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for4([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            uint32_t nz[L];
+            ns.template words<c>(nz);
             float lc[L];
 #pragma unroll
             for (int k = 0; k < L; ++k) lc[k] = l[k][c];
             Relaxed<GRID> r;
-            relax_coord<GRID>(lc, &nz[c * L], static_cast<int>((cw >> (8 * c)) & 0xFF), tk_next, r);
+            relax_coord<GRID>(lc, nz, static_cast<int>((cw >> (8 * c)) & 0xFF), tk_next, r);
             out[c] = sn * r.what;
-        }
+        });
         uint2 o;
         o.x = pack_bf16x2(out[0] - w[0], out[1] - w[1]);
         o.y = pack_bf16x2(out[2] - w[2], out[3] - w[3]);
-        *reinterpret_cast<uint2*>(dW + i0) = o;
+        *reinterpret_cast<uint2*>(ix.at(dW)) = o;
     }
 }
 
@@ -245,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void init_rtn_kernel(const void* __restri
     const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
     if (i0 >= mk) return;
     float w[4];
-    load_w4(W, WBF16, i0, w);
+    load_w4(W, WBF16, Idx<false>{i0}, w);
     float amax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
     amax = group32_max(amax);
     const float s = __fdiv_rn(amax, qmax);
@@ -386,17 +429,23 @@ hipError_t launch_init_rtn(const LayerDesc& d, const void* W, float* scales, uin
     return hipGetLastError();
 }
 
+// Offsets fit 32 bits when every byte offset into an fp32 [rows][cols]
+// plane does.
+inline bool off32(const LayerDesc& d) { return d.mk * 4 <= 0xFFFFFFF0ull; }
+
 hipError_t launch_relax_fwd(const LayerDesc& d, const float* logits, const float* scales,
                             const uint8_t* codes, const void* W, uint32_t step, TauK tk,
                             uint16_t* dW, float* w_soft_dbg, hipStream_t st) {
     const unsigned nb = blocks_for(d.mk / 4);
-#define GSQ_FWD(G, WB, DB) \
-    GSQ_LAUNCH((relax_fwd_kernel<G, WB, DB>), nb, st, logits, scales, codes, W, d.mk, step, d.sid, d.key, tk, dW, w_soft_dbg)
+    const bool o32 = off32(d);
+#define GSQ_FWD(G, WB, DB, O) \
+    GSQ_LAUNCH((relax_fwd_kernel<G, WB, DB, O>), nb, st, logits, scales, codes, W, d.mk, step, d.sid, d.key, tk, dW, w_soft_dbg)
+#define GSQ_FWD_O(G, WB, DB) if (o32) GSQ_FWD(G, WB, DB, true); else GSQ_FWD(G, WB, DB, false);
 #define GSQ_FWD_G(G)                                       \
     if (d.w_bf16) {                                        \
-        if (w_soft_dbg) GSQ_FWD(G, true, true); else GSQ_FWD(G, true, false);   \
+        if (w_soft_dbg) { GSQ_FWD_O(G, true, true); } else { GSQ_FWD_O(G, true, false); }   \
     } else {                                               \
-        if (w_soft_dbg) GSQ_FWD(G, false, true); else GSQ_FWD(G, false, false); \
+        if (w_soft_dbg) { GSQ_FWD_O(G, false, true); } else { GSQ_FWD_O(G, false, false); } \
     }
     switch (d.grid) {
         case GSQ_GRID_INT2: GSQ_FWD_G(GSQ_GRID_INT2); break;
@@ -404,6 +453,7 @@ hipError_t launch_relax_fwd(const LayerDesc& d, const float* logits, const float
         default: GSQ_FWD_G(GSQ_GRID_INT3_LOCAL); break;
     }
 #undef GSQ_FWD_G
+#undef GSQ_FWD_O
 #undef GSQ_FWD
     return hipGetLastError();
 }
@@ -416,18 +466,21 @@ hipError_t launch_relax_bwd_lion(const LayerDesc& d, const float* G, float* logi
     const unsigned nb = blocks_for(d.mk / 4);
     const bool dbg = gl_dbg != nullptr || gs_dbg != nullptr;
     const bool fwd = dW != nullptr;
-#define GSQ_BWD(G_, DB, FW, WB) \
-    GSQ_LAUNCH((relax_bwd_lion_kernel<G_, DB, FW, WB>), nb, st, G, logits, mom, scales, scale_mom, codes, d.mk, step, d.sid, d.key, tk, lkl, lks, gl_dbg, gs_dbg, W, next_step, tk_next, dW)
-#define GSQ_BWD_G(G_)                                                   \
-    if (!fwd) { if (dbg) GSQ_BWD(G_, true, false, true); else GSQ_BWD(G_, false, false, true); } \
-    else if (d.w_bf16) GSQ_BWD(G_, false, true, true);                  \
-    else GSQ_BWD(G_, false, true, false);
+    const bool o32 = off32(d);
+#define GSQ_BWD(G_, DB, FW, WB, O) \
+    GSQ_LAUNCH((relax_bwd_lion_kernel<G_, DB, FW, WB, O>), nb, st, G, logits, mom, scales, scale_mom, codes, d.mk, step, d.sid, d.key, tk, lkl, lks, gl_dbg, gs_dbg, W, next_step, tk_next, dW)
+#define GSQ_BWD_O(G_, DB, FW, WB) if (o32) GSQ_BWD(G_, DB, FW, WB, true); else GSQ_BWD(G_, DB, FW, WB, false);
+#define GSQ_BWD_G(G_)                                                            \
+    if (!fwd) { if (dbg) { GSQ_BWD_O(G_, true, false, true); } else { GSQ_BWD_O(G_, false, false, true); } } \
+    else if (d.w_bf16) { GSQ_BWD_O(G_, false, true, true); }                     \
+    else { GSQ_BWD_O(G_, false, true, false); }
     switch (d.grid) {
         case GSQ_GRID_INT2: GSQ_BWD_G(GSQ_GRID_INT2); break;
         case GSQ_GRID_TERNARY: GSQ_BWD_G(GSQ_GRID_TERNARY); break;
         default: GSQ_BWD_G(GSQ_GRID_INT3_LOCAL); break;
     }
 #undef GSQ_BWD_G
+#undef GSQ_BWD_O
 #undef GSQ_BWD
     return hipGetLastError();
 }
