@@ -1,0 +1,185 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times, on sampled rows the oracle computes one by one (every kernel of the
+step is row-local except the two products, whose sampled rows the oracle forms
+from the GPU's own bf16 operands), plus properties that hold at any size.
+Also: the step is deterministic (two runs from the same state are identical)."""
+
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests.gpu_util import device, to_dev_bf16, bf16_values, f32, bf16_ulp, report
+
+pytestmark = pytest.mark.gpu
+
+WORKLOADS = ["linear512_int2", "qproj4096_int2", "downproj4096x14336_ternary",
+             "gateproj28672x8192_int3local", "moe64x2048x7168_int2"]
+
+
+def _sample_rows(M, rpe, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, M // 2, M - 1, rpe - 1, min(rpe, M - 1)}
+    rows |= set(int(r) for r in rng.integers(0, M, 4))
+    return sorted(rows)
+
+
+def _log(msg):
+    print(f"[fullsize] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_fullsize_sampled_parity(name):
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver
+    dev = device()
+    t0 = time.time()
+    d = synthetic.generate(name, seed=0)
+    wl = d["workload"]
+    grid = wl.grid
+    _log(f"{name}: inputs drawn in {time.time() - t0:.1f} s")
+    Wd = to_dev_bf16(d["W_bits"], dev) if d["W_bits"] is not None else torch.from_numpy(d["W"]).to(dev)
+    Xd = to_dev_bf16(d["X_bits"], dev)
+    E = wl.experts
+    rpe = wl.rows_per_expert or wl.rows
+    lion = g.GsqLion.make(lr_logit=wl.lr_logit, lr_scale=1e-5)
+    sol = LayerSolver(Wd, Xd, grid, tok_offsets=d["tok_offsets"], rows_per_expert=rpe, seed=0,
+                      stream_id=0, lion=lion)
+    M, K = sol.rows, sol.cols
+    L = oracle.N_LOGITS[grid]
+    rows = _sample_rows(M, rpe)
+    W = d["W"]
+    X = d["X"].astype(np.float64)
+    offs = [int(o) for o in d["tok_offsets"]]          # unpadded
+    poffs = [int(o) for o in sol.tok_offsets]          # padded to 64 on the device
+
+    # --- warm start: bit-exact on sampled rows ---
+    torch.cuda.synchronize()
+    s_ref, c_ref, l_ref = oracle.init_rtn(W[rows], grid)
+    np.testing.assert_array_equal(f32(sol.scales[rows]).view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(sol.codes[rows].cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(f32(sol.logits[:, rows]).view(np.uint32), l_ref.view(np.uint32))
+    _log(f"{name}: init ok ({M}x{K}, {L} logits)")
+
+    # --- relaxed forward at step 0 ---
+    tau, step = 0.5, 0
+    w_soft = torch.empty((M, K), dtype=torch.float32, device=dev)
+    sol.relax_fwd(step, tau, 1.0, w_soft)
+    torch.cuda.synchronize()
+    ws_rows = f32(w_soft[rows])
+    dW_rows = bf16_values(sol.dW[rows]).astype(np.float64)
+    for j, r in enumerate(rows):
+        ref = oracle.relax_fwd(l_ref[:, j:j + 1], s_ref[j:j + 1], W[r:r + 1], grid, 0, 0, step, tau,
+                               1.0, c_ref[j:j + 1], row0=r)
+        nat = np.repeat(s_ref[j:j + 1].astype(np.float64), 128, axis=1) * oracle.Q_MAX[grid]
+        assert np.all(np.abs(ws_rows[j] - ref["w_soft"][0]) <= 1e-5 * np.maximum(nat[0], 1e-30))
+        assert np.all(np.abs(dW_rows[j] - ref["dW"][0]) <= bf16_ulp(ref["dW"][0]) + 1e-5 * nat[0])
+    _log(f"{name}: relax_fwd ok on rows {rows}")
+
+    # --- objective and gradient ---
+    sol.recon()
+    torch.cuda.synchronize()
+    loss = float(sol.loss.item())
+    RT = sol.RT
+    G_rows = f32(sol.G[rows]).astype(np.float64)
+    exact_rows_loss = gpu_rows_loss = 0.0
+    for j, r in enumerate(rows):
+        e = r // rpe
+        n, pn = offs[e + 1] - offs[e], poffs[e + 1] - poffs[e]
+        Xe = X[offs[e]:offs[e + 1]]
+        base = rpe * poffs[e] + (r - e * rpe) * pn
+        rt = bf16_values(RT[base:base + pn]).astype(np.float64)
+        assert not rt[n:].any()                      # padded tokens contribute zero
+        rt = rt[:n]
+        rt_ref = Xe @ dW_rows[j]                     # exact from the GPU's bf16 operands
+        gam = (K + 2) * 2.0 ** -24 * (np.abs(Xe) @ np.abs(dW_rows[j]))
+        assert np.all(np.abs(rt - rt_ref) <= 0.5 * bf16_ulp(rt_ref) + gam + 1e-30)
+        g_ref = 2.0 * rt @ Xe
+        gb = (n + 2) * 2.0 ** -24 * 2.0 * (np.abs(rt) @ np.abs(Xe))
+        assert np.all(np.abs(G_rows[j] - g_ref) <= gb + 1e-30)
+        ref = oracle.relax_fwd(l_ref[:, j:j + 1], s_ref[j:j + 1], W[r:r + 1], grid, 0, 0, step, tau,
+                               1.0, c_ref[j:j + 1], row0=r)
+        exact_rows_loss += float(np.sum((Xe @ ref["dW"][0]) ** 2))
+        gpu_rows_loss += float(np.sum(rt_ref ** 2))
+    # exact-mode loss of the sampled rows (unrounded fp64 dW) against the
+    # rows' loss from the GPU's bf16 dW: the rounding may move it by <= 2e-3.
+    rel_exact = abs(gpu_rows_loss - exact_rows_loss) / exact_rows_loss
+    # whole-layer property: the loss equals the sum of squares of R^T up to
+    # R^T's bf16 rounding (the loss is taken before it).
+    rt_all = bf16_values(RT).astype(np.float64)
+    rel_rt = abs(float(np.sum(rt_all * rt_all)) - loss) / loss
+    report(f"{name} recon", loss=loss, rel_vs_exact_rows=rel_exact, rel_vs_sum_RT2=rel_rt)
+    assert rel_exact <= 2e-3
+    assert rel_rt <= 1e-3
+    del rt_all
+    _log(f"{name}: recon ok")
+
+    # --- backward + Lion on a copy (debug gradients), then the fused pass ---
+    Gh = G_rows
+    keep = [x.clone() for x in (sol.logits, sol.mom, sol.scales, sol.scale_mom)]
+    gl = torch.empty_like(sol.logits)
+    gs = torch.empty_like(sol.scales)
+    g.gsq_relax_bwd_lion(sol.layer, sol.G, keep[0], keep[1], keep[2], keep[3], sol.init_codes,
+                         step, tau, 1.0, lion, gl, gs)
+    torch.cuda.synchronize()
+    gl_rows = f32(gl[:, rows])
+    gs_rows = f32(gs[rows])
+    for j, r in enumerate(rows):
+        glr, gsr = oracle.relax_bwd(Gh[j:j + 1], l_ref[:, j:j + 1], s_ref[j:j + 1], grid, 0, 0, step,
+                                    tau, 1.0, c_ref[j:j + 1], row0=r)
+        nat = np.abs(Gh[j]) * np.repeat(s_ref[j].astype(np.float64), 128) * oracle.Q_MAX[grid] / tau
+        assert np.all(np.abs(gl_rows[:, j] - glr[:, 0]) <= 1e-5 * nat[None] + 1e-30)
+        f = oracle.relax_fwd(l_ref[:, j:j + 1], s_ref[j:j + 1], W[r:r + 1], grid, 0, 0, step, tau, 1.0,
+                             c_ref[j:j + 1], row0=r)
+        mass = (np.abs(Gh[j]) * np.abs(f["w_hat"][0])).reshape(-1, 128).sum(1)
+        gabs = np.abs(Gh[j]).reshape(-1, 128).sum(1)
+        assert np.all(np.abs(gs_rows[j] - gsr[0]) <= 130 * 2.0 ** -24 * mass + 1e-5 * oracle.Q_MAX[grid] * gabs)
+    th, _ = oracle.lion(l_ref, gl_rows, np.zeros_like(l_ref), wl.lr_logit, 0.9, 0.99)
+    np.testing.assert_array_equal(f32(keep[0][:, rows]).view(np.uint32), th.view(np.uint32))
+    _log(f"{name}: relax_bwd_lion ok")
+    # the fused pass equals backward + Lion followed by the next forward
+    dW_sep = torch.empty_like(sol.dW)
+    g.gsq_relax_fwd(sol.layer, keep[0], keep[2], sol.init_codes, sol.W, step + 1, 0.45, 1.0, dW_sep)
+    sol.relax_bwd_lion_fwd(step, tau, step + 1, 0.45)
+    torch.cuda.synchronize()
+    for a, b in zip((sol.logits, sol.mom, sol.scales, sol.scale_mom, sol.dW),
+                    (keep[0], keep[1], keep[2], keep[3], dW_sep)):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    _log(f"{name}: fused pass bit-identical")
+
+    # --- harden + pack on sampled rows ---
+    codes, packed, s16 = sol.harden()
+    torch.cuda.synchronize()
+    lg_rows = f32(sol.logits[:, rows])
+    c0_rows = sol.codes[rows].cpu().numpy()
+    cr, pr, sr = oracle.harden_pack(lg_rows, f32(sol.scales[rows]), grid, c0_rows)
+    np.testing.assert_array_equal(codes[rows].cpu().numpy(), cr)
+    np.testing.assert_array_equal(packed[rows].cpu().numpy().view(np.uint32), pr)
+    np.testing.assert_array_equal(s16[rows].cpu().numpy().view(np.uint16), sr)
+    _log(f"{name}: harden_pack ok; {time.time() - t0:.1f} s total")
+
+
+def test_step_is_deterministic():
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver
+    dev = device()
+    d = synthetic.generate("qproj4096_int2", seed=0)
+    Wd = to_dev_bf16(d["W_bits"], dev)
+    Xd = to_dev_bf16(d["X_bits"], dev)
+    results = []
+    for _ in range(2):
+        sol = LayerSolver(Wd, Xd, g.GRID_INT2, seed=3, stream_id=2)
+        sol.relax_fwd(0, 1.0)
+        for t in range(3):
+            sol.step_fused(t, 1.0 - 0.1 * t, 0.9 - 0.1 * t)
+        torch.cuda.synchronize()
+        results.append([sol.logits.clone(), sol.mom.clone(), sol.scales.clone(), sol.G.clone(),
+                        sol.dW.view(torch.int16).clone(), sol.loss.clone()])
+        del sol
+    for a, b in zip(*results):
+        assert torch.equal(a, b)
