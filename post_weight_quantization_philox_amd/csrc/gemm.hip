@@ -148,14 +148,16 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
     const int rowA = wi * 128 + frow;
     const int rowB = wj * 128 + frow;
 
-    bf16x8 fa[2][4], fb[2][4];
+    // Fragment registers: one slot per 16-wide slice of the K-step (slice kk
+    // always lives in slot kk), fetched two slices ahead of its MFMAs.
+    bf16x8 fa[4][4], fb[4][4];
     auto read_a = [&](const uint4* t, int kk, int b) {
         return __builtin_bit_cast(bf16x8, t[(rowA + 32 * b) * kChunks + ((2 * kk + fhalf) ^ fsw)]);
     };
     auto read_b = [&](const uint4* t, int kk, int b) {
         return __builtin_bit_cast(bf16x8, t[(rowB + 32 * b) * kChunks + ((2 * kk + fhalf) ^ fsw)]);
     };
-    // DMA load d (0..15) of the next K-step: A loads q = 0..7, then B.
+    // DMA load d (0..15) of a K-step: A loads q = 0..7, then B.
     auto dma1 = [&](int d, uint32_t koff, uint4* nA, uint4* nB) {
         const int q = d & 7;
         const int r0 = 8 * (4 * q + wave);
@@ -166,55 +168,53 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rs, (lds_void*)(nB + r0 * kChunks), 16,
                                                      ob[q] + koff, 0, 0, 0);
     };
-
-    // Fragment reads of one slice, in the order the next slice consumes
-    // them: B blocks 0-1, B 2-3, A 0-1, A 2-3 (two per sub-group), so a
-    // block's MFMAs never wait on a read issued just before them.
-    auto fetch2 = [&](const uint4* tA, const uint4* tB, int kk, int slot, int part) {
+    // Two of the eight fragment reads of slice kk into its slot, in the
+    // order its MFMAs consume them: B blocks 0-1, B 2-3, A 0-1, A 2-3.
+    auto fetch2 = [&](const uint4* tA, const uint4* tB, int kk, int part) {
         if (part < 2) {
-            fb[slot][2 * part] = read_b(tB, kk, 2 * part);
-            fb[slot][2 * part + 1] = read_b(tB, kk, 2 * part + 1);
+            fb[kk][2 * part] = read_b(tB, kk, 2 * part);
+            fb[kk][2 * part + 1] = read_b(tB, kk, 2 * part + 1);
         } else {
-            fa[slot][2 * part - 4] = read_a(tA, kk, 2 * part - 4);
-            fa[slot][2 * part - 3] = read_a(tA, kk, 2 * part - 3);
+            fa[kk][2 * part - 4] = read_a(tA, kk, 2 * part - 4);
+            fa[kk][2 * part - 3] = read_a(tA, kk, 2 * part - 3);
         }
     };
 
-    // One K-step, issued as 16 sub-groups (slice kk, A block a): two
-    // fragment reads for the next slice, two DMA loads of the next K-step
-    // (first two slices only, so they land before they are needed), and the
-    // 4 MFMAs of block a. The scheduling barriers keep this order, so memory
-    // instructions drain between MFMAs instead of blocking them in a burst.
-    // Halfway through the last slice the wave syncs with the others on the
-    // next buffer and fetches that buffer's first slice (B, then A), so the
-    // next step starts with its fragments in flight.
-    auto kstep = [&](auto has_next, const uint4* tA, const uint4* tB, uint4* nA, uint4* nB,
-                     uint32_t knext) {
-        constexpr bool kNext = decltype(has_next)::value;
+    // One K-step, issued as 16 sub-groups (slice kk, A block a) of two
+    // fragment reads and the 4 MFMAs of block a, pinned in this order by
+    // scheduling barriers so memory instructions drain between MFMAs.
+    // Slices 0-1 fetch slices 2-3 of this step. At the start of slice 2 all
+    // reads of this step's buffer are issued: after they land, the next
+    // step's buffer has landed, and the workgroup has synced, slices 2-3
+    // fetch slices 0-1 of the next step and load step k+2 into this step's
+    // buffer (two DMA loads per sub-group), about a full K-step ahead.
+    auto kstep = [&](auto has_next, auto has_next2, const uint4* tA, const uint4* tB,
+                     const uint4* nA, const uint4* nB, uint32_t knext2) {
+        constexpr bool kNext = decltype(has_next)::value;    // step k+1 exists
+        constexpr bool kNext2 = decltype(has_next2)::value;  // step k+2 exists
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const int cur = kk & 1, nxt = cur ^ 1;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                if constexpr (kNext) {
-                    if (kk < 2) {
-                        dma1(2 * (4 * kk + a), knext, nA, nB);
-                        dma1(2 * (4 * kk + a) + 1, knext, nA, nB);
-                    }
-                    if (kk == 3 && a == 2) {
+                if (kk < 2) {
+                    fetch2(tA, tB, kk + 2, a);
+                } else if constexpr (kNext) {
+                    if (kk == 2 && a == 0) {
                         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                         wait_dma();
                         bar();
                     }
-                    if (kk == 3 && a >= 2) {
-                        fetch2(nA, nB, 0, 0, 2 * (a - 2));
-                        fetch2(nA, nB, 0, 0, 2 * (a - 2) + 1);
+                    fetch2(nA, nB, kk - 2, a);
+                    if constexpr (kNext2) {
+                        uint4* fA = const_cast<uint4*>(tA);
+                        uint4* fB = const_cast<uint4*>(tB);
+                        dma1(2 * (4 * (kk - 2) + a), knext2, fA, fB);
+                        dma1(2 * (4 * (kk - 2) + a) + 1, knext2, fA, fB);
                     }
                 }
-                if (kk < 3) fetch2(tA, tB, kk + 1, nxt, a);
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b],
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][a], fb[kk][b],
                                                                         acc[a][b], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -223,23 +223,39 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
 
     const int nk = g.Rd / BK;
     constexpr uint32_t kStep = BK * 2;   // bytes of one K-step along a row
+    // Prologue: step 0 (waited for) and step 1 in flight; slices 0-1 fetched.
     dma_tile(ra_rs, oa, 0, sA0, wave);
     dma_tile(rb_rs, ob, 0, sB0, wave);
-    wait_dma();
+    if (nk > 1) {
+        wait_dma();
+        dma_tile(ra_rs, oa, kStep, sA1, wave);
+        dma_tile(rb_rs, ob, kStep, sB1, wave);
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+        wait_dma();
+    }
     bar();
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        fa[0][b] = read_a(sA0, 0, b);
-        fb[0][b] = read_b(sB0, 0, b);
+    for (int part = 0; part < 4; ++part) {
+        fetch2(sA0, sB0, 0, part);
+        fetch2(sA0, sB0, 1, part);
     }
-    for (int kt = 0; kt + 1 < nk; ++kt) {
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) {
         const bool odd = kt & 1;
-        kstep(std::true_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1,
-              static_cast<uint32_t>(kt + 1) * kStep);
+        kstep(std::true_type{}, std::true_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0,
+              odd ? sA0 : sA1, odd ? sB0 : sB1, static_cast<uint32_t>(kt + 2) * kStep);
+    }
+    if (kt + 1 < nk) {
+        const bool odd = kt & 1;
+        kstep(std::true_type{}, std::false_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0,
+              odd ? sA0 : sA1, odd ? sB0 : sB1, 0u);
+        ++kt;
     }
     {
-        const bool odd = (nk - 1) & 1;
-        kstep(std::false_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0, nullptr, nullptr, 0u);
+        const bool odd = kt & 1;
+        kstep(std::false_type{}, std::false_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0, nullptr,
+              nullptr, 0u);
     }
     // All waves are done with the operand buffers before the epilogue reuses them.
     __syncthreads();
@@ -247,8 +263,8 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
     // Epilogue, one 32-row slab of the wave's 128x128 sub-tile at a time:
     // accumulators go to a private 32x128 fp32 LDS slab (register r of block
     // (a, b) is C[8*(r/4) + 4*(lane/32) + r%4][32*b + lane%32]), then each
-    // lane reads back 8 consecutive values of one row and stores them as one
-    // 16-byte (bf16) or two 16-byte (fp32) vectors. N and K are multiples of
+    // lane reads back 8 (bf16 output) or 4 (fp32 output) consecutive values of
+    // one row and stores them as one 16-byte vector. N and K are multiples of
     // 8, so a vector is entirely inside or outside the matrix.
     constexpr int kSlab = 128 + 4;      // padded row: the two half-waves' rows
                                         // start 16 bytes apart in the banks
@@ -268,16 +284,17 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
             }
         }
         __syncthreads();
+        if constexpr (EPI == EPI_BF16_LOSS) {
+            // 16 lanes per 128-value row: 8 values -> one 16-byte bf16 store.
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int c = lane + 64 * t;          // 512 chunks of 8 values
-            const int row = c >> 4, col = (c & 15) * 8;
-            const float4 v0 = *reinterpret_cast<const float4*>(slab + row * kSlab + col);
-            const float4 v1 = *reinterpret_cast<const float4*>(slab + row * kSlab + col + 4);
-            const int grow = grow0 + a * 32 + row, gcol = gcol0 + col;
-            if (grow < g.I && gcol < g.J) {
-                const int64_t off = static_cast<int64_t>(grow) * g.ldc + gcol;
-                if constexpr (EPI == EPI_BF16_LOSS) {
+            for (int t = 0; t < 8; ++t) {
+                const int c = lane + 64 * t;
+                const int row = c >> 4, col = (c & 15) * 8;
+                const float4 v0 = *reinterpret_cast<const float4*>(slab + row * kSlab + col);
+                const float4 v1 = *reinterpret_cast<const float4*>(slab + row * kSlab + col + 4);
+                const int grow = grow0 + a * 32 + row, gcol = gcol0 + col;
+                if (grow < g.I && gcol < g.J) {
+                    const int64_t off = static_cast<int64_t>(grow) * g.ldc + gcol;
                     lsum = __builtin_fmaf(v0.x, v0.x, lsum); lsum = __builtin_fmaf(v0.y, v0.y, lsum);
                     lsum = __builtin_fmaf(v0.z, v0.z, lsum); lsum = __builtin_fmaf(v0.w, v0.w, lsum);
                     lsum = __builtin_fmaf(v1.x, v1.x, lsum); lsum = __builtin_fmaf(v1.y, v1.y, lsum);
@@ -286,12 +303,21 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
                     o.x = pack_bf16x2(v0.x, v0.y); o.y = pack_bf16x2(v0.z, v0.w);
                     o.z = pack_bf16x2(v1.x, v1.y); o.w = pack_bf16x2(v1.z, v1.w);
                     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C) + off) = o;
-                } else {
-                    float* dst = static_cast<float*>(g.C) + off;
-                    *reinterpret_cast<float4*>(dst) =
-                        make_float4(g.alpha * v0.x, g.alpha * v0.y, g.alpha * v0.z, g.alpha * v0.w);
-                    *reinterpret_cast<float4*>(dst + 4) =
-                        make_float4(g.alpha * v1.x, g.alpha * v1.y, g.alpha * v1.z, g.alpha * v1.w);
+                }
+            }
+        } else {
+            // 32 lanes per 128-value row: each store instruction writes two
+            // whole 512-byte rows.
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int c = lane + 64 * t;
+                const int row = c >> 5, col = (c & 31) * 4;
+                const float4 v = *reinterpret_cast<const float4*>(slab + row * kSlab + col);
+                const int grow = grow0 + a * 32 + row, gcol = gcol0 + col;
+                if (grow < g.I && gcol < g.J) {
+                    const int64_t off = static_cast<int64_t>(grow) * g.ldc + gcol;
+                    *reinterpret_cast<float4*>(static_cast<float*>(g.C) + off) =
+                        make_float4(g.alpha * v.x, g.alpha * v.y, g.alpha * v.z, g.alpha * v.w);
                 }
             }
         }

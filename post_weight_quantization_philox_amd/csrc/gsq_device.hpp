@@ -49,33 +49,25 @@ __device__ __forceinline__ void philox_block(uint64_t blk, uint32_t step, uint32
     out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
 }
 
-// Noise words of the four coordinates i0..i0+3 (i0 % 4 == 0) of a grid with L
-// logits: stream elements e = i*L + k, i.e. the L whole blocks starting at
-// block i0*L/4. Word c*L + k belongs to coordinate i0 + c, logit k.
-template <int L>
-__device__ __forceinline__ void noise_words4(uint64_t i0, uint32_t step, uint32_t sid, Key key,
-                                             uint32_t w[4 * L]) {
-    const uint64_t b0 = (i0 >> 2) * L;
-#pragma unroll
-    for (int j = 0; j < L; ++j) philox_block(b0 + j, step, sid, key, &w[4 * j]);
-}
-
-// Lazy form of noise_words4: coordinate C (0..3) of the four starting at i0
-// takes words C*L .. C*L + L - 1 of the same block sequence. Blocks are
+// Noise of the N consecutive coordinates i0..i0+N-1 of a grid with L logits
+// (N*L a multiple of 4, i0 a multiple of N): stream elements e = i*L + k, i.e.
+// the N*L/4 whole Philox blocks starting at block i0*L/4. Coordinate C
+// (0..N-1) takes words C*L .. C*L + L - 1 of that block sequence. Blocks are
 // generated on demand, in order, with at most two live (the last two), so the
-// words of all four coordinates never occupy registers at once. Which blocks
-// are new for coordinate C is known at compile time.
-template <int L>
-struct NoiseStream4 {
+// words of all N coordinates never occupy registers at once. Which blocks are
+// new for coordinate C is known at compile time.
+template <int L, int N>
+struct NoiseStream {
+    static_assert((L * N) % 4 == 0, "coordinates per thread must cover whole Philox blocks");
     uint64_t b0;
     uint32_t step, sid;
     Key key;
     uint32_t cur[4], nxt[4];   // after words<C>(): blocks hi(C) - 1 and hi(C)
 
-    __device__ __forceinline__ NoiseStream4(uint64_t i0, uint32_t step_, uint32_t sid_, Key key_)
-        : b0((i0 >> 2) * L), step(step_), sid(sid_), key(key_) {}
+    __device__ __forceinline__ NoiseStream(uint64_t i0, uint32_t step_, uint32_t sid_, Key key_)
+        : b0((i0 * L) >> 2), step(step_), sid(sid_), key(key_) {}
 
-    // Calls must come in order C = 0, 1, 2, 3.
+    // Calls must come in order C = 0, 1, ..., N - 1.
     template <int C>
     __device__ __forceinline__ void words(uint32_t (&w)[L]) {
         constexpr int first = C * L;
@@ -145,22 +137,30 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Reductions within the 32 lanes that share a scale group (lanes 0-31 and
-// 32-63 of a wave hold two different groups). Butterfly: every lane ends with
-// the full result; callers let one fixed lane write it, so the stored value is
-// deterministic.
+// Reductions within the P lanes (P = 32 or 64) that share a scale group: with
+// 4 coordinates per thread the two halves of a wave hold two groups, with 2
+// the whole wave holds one. Butterfly: every lane ends with the full result;
+// callers let one fixed lane write it, so the stored value is deterministic.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float group32_sum(float v) {
+template <int P>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(P == 32 || P == 64, "a scale group spans half a wave or a whole wave");
 #pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    for (int m = P / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
 }
 
-__device__ __forceinline__ float group32_max(float v) {
+template <int P>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(P == 32 || P == 64, "a scale group spans half a wave or a whole wave");
 #pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    for (int m = P / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
     return v;
 }
+
+// First lane of the P-lane group that holds this lane.
+template <int P>
+__device__ __forceinline__ int group_lane0() { return static_cast<int>(threadIdx.x) & (64 - P); }
 
 // Lion on one fp32 parameter (Chen et al. 2023). The sign is taken on
 // c = fma(beta1, m, fp32((1-beta1)*g)); theta <- theta - lr*sign(c) - lr*wd*theta;

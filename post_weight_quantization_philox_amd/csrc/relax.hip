@@ -1,13 +1,14 @@
 // Elementwise and group-reduction kernels of the GSQ step (gfx950).
 //
-// Thread mapping shared by the forward, backward and warm-start kernels: one
-// thread owns four consecutive coordinates i0..i0+3 of the flattened layer
-// (i0 = 4 * global thread id), so every planar logit / momentum plane is read
-// and written as one 16-byte vector per thread and a wave touches 1 KiB of
-// each plane per instruction. 32 threads cover one scale group of 128
-// coordinates; the two halves of a wave are two groups, reduced with lane
-// shuffles. The four coordinates' noise is a whole number of Philox blocks
-// (L blocks for L logits), so no word is generated twice.
+// Thread mapping shared by the forward and backward kernels: one thread owns
+// N consecutive coordinates i0..i0+N-1 of the flattened layer (i0 = N * global
+// thread id), so every planar logit / momentum plane is read and written as
+// one N*4-byte vector per thread. 128/N threads cover one scale group of 128
+// coordinates and reduce it with lane shuffles. N is 2 for the 2-bit grid
+// (halving the registers a thread holds, so that more waves are in flight
+// to hide HBM latency) and 4 for ternary (already at full occupancy) and local
+// shift (whose 5 logits need N = 4 for the N coordinates' noise to be a whole
+// number of Philox blocks, L*N/4, so that no word is generated twice).
 #include <type_traits>
 
 #include "gsq_internal.hpp"
@@ -19,9 +20,11 @@ namespace {
 constexpr int kThreads = 256;
 
 template <int GRID> struct GridT;
-template <> struct GridT<GSQ_GRID_INT2> { static constexpr int L = 4; static constexpr int QMAX = 3; static constexpr int BITS = 2; };
-template <> struct GridT<GSQ_GRID_TERNARY> { static constexpr int L = 2; static constexpr int QMAX = 1; static constexpr int BITS = 2; };
-template <> struct GridT<GSQ_GRID_INT3_LOCAL> { static constexpr int L = 5; static constexpr int QMAX = 7; static constexpr int BITS = 3; };
+// L logits per coordinate, q_max, code bits, and N coordinates per thread in
+// the relax kernels.
+template <> struct GridT<GSQ_GRID_INT2> { static constexpr int L = 4; static constexpr int QMAX = 3; static constexpr int BITS = 2; static constexpr int N = 2; };
+template <> struct GridT<GSQ_GRID_TERNARY> { static constexpr int L = 2; static constexpr int QMAX = 1; static constexpr int BITS = 2; static constexpr int N = 4; };
+template <> struct GridT<GSQ_GRID_INT3_LOCAL> { static constexpr int L = 5; static constexpr int QMAX = 7; static constexpr int BITS = 3; static constexpr int N = 4; };
 
 // Element i of a tensor whose planes start at wave-uniform bases. With O32
 // the byte offset of i fits 32 bits (checked by the launcher: rows*cols*4 <
@@ -54,6 +57,77 @@ __device__ __forceinline__ void load_w4(const void* W, bool bf16, Idx<O32> ix, f
     }
 }
 
+// Streaming accesses. Every logit, momentum, G, W and dW element is touched
+// once per launch, so the relax kernels load and store them nontemporally
+// (no reuse to keep in the caches); on the fused pass's mix of nine read and
+// eight write streams this is worth about an eighth of the HBM time.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void st_nt(T v, T* p) { __builtin_nontemporal_store(v, p); }
+
+// N = 2 or 4 consecutive values as one vector access.
+template <int N>
+__device__ __forceinline__ void loadv(const float* p, float (&v)[N]) {
+    if constexpr (N == 4) {
+        const f32x4_t x = ld_nt(reinterpret_cast<const f32x4_t*>(p));
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+        static_assert(N == 2, "2 or 4 coordinates per thread");
+        const f32x2_t x = ld_nt(reinterpret_cast<const f32x2_t*>(p));
+        v[0] = x.x; v[1] = x.y;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void storev(float* p, const float (&v)[N]) {
+    if constexpr (N == 4) {
+        st_nt(f32x4_t{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4_t*>(p));
+    } else {
+        st_nt(f32x2_t{v[0], v[1]}, reinterpret_cast<f32x2_t*>(p));
+    }
+}
+
+template <int N, bool O32>
+__device__ __forceinline__ void load_w(const void* W, bool bf16, Idx<O32> ix, float (&w)[N]) {
+    if (bf16) {
+        const uint16_t* p = ix.at(static_cast<const uint16_t*>(W));
+        if constexpr (N == 4) {
+            const u32x2_t v = ld_nt(reinterpret_cast<const u32x2_t*>(p));
+            w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x); w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
+        } else {
+            const uint32_t v = ld_nt(reinterpret_cast<const uint32_t*>(p));
+            w[0] = bf16_lo(v); w[1] = bf16_hi(v);
+        }
+    } else {
+        loadv<N>(ix.at(static_cast<const float*>(W)), w);
+    }
+}
+
+// The N warm-start codes (one byte each) as one little-endian word.
+template <int N, bool O32>
+__device__ __forceinline__ uint32_t load_codes(const uint8_t* codes, Idx<O32> ix) {
+    if constexpr (N == 4) return ld_nt(reinterpret_cast<const uint32_t*>(ix.at(codes)));
+    else return ld_nt(reinterpret_cast<const uint16_t*>(ix.at(codes)));
+}
+
+// dW = out - w for the N coordinates, rounded to bf16 and stored as one vector.
+template <int N, bool O32>
+__device__ __forceinline__ void store_dw(uint16_t* dW, Idx<O32> ix, const float (&out)[N],
+                                         const float (&w)[N]) {
+    if constexpr (N == 4) {
+        const u32x2_t o = {pack_bf16x2(out[0] - w[0], out[1] - w[1]),
+                           pack_bf16x2(out[2] - w[2], out[3] - w[3])};
+        st_nt(o, reinterpret_cast<u32x2_t*>(ix.at(dW)));
+    } else {
+        st_nt(pack_bf16x2(out[0] - w[0], out[1] - w[1]), reinterpret_cast<uint32_t*>(ix.at(dW)));
+    }
+}
+
 __device__ __forceinline__ void load4(const float* p, float v[4]) {
     const float4 x = *reinterpret_cast<const float4*>(p);
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
@@ -65,10 +139,11 @@ __device__ __forceinline__ void store4(float* p, const float v[4]) {
 
 template <int C> using Ci = std::integral_constant<int, C>;
 
-// Calls f(Ci<0>{}) .. f(Ci<3>{}) in order.
-template <typename F>
-__device__ __forceinline__ void for4(F&& f) {
-    f(Ci<0>{}); f(Ci<1>{}); f(Ci<2>{}); f(Ci<3>{});
+// Calls f(Ci<0>{}) .. f(Ci<N-1>{}) in order (N = 2 or 4).
+template <int N, typename F>
+__device__ __forceinline__ void forN(F&& f) {
+    f(Ci<0>{}); f(Ci<1>{});
+    if constexpr (N == 4) { f(Ci<2>{}); f(Ci<3>{}); }
 }
 
 // Candidate value (scale units) of local-shift logit k around code c0:
@@ -140,20 +215,21 @@ __global__ __launch_bounds__(kThreads) void relax_fwd_kernel(
     const uint8_t* __restrict__ codes, const void* __restrict__ W, uint64_t mk, uint32_t step,
     uint32_t sid, Key key, TauK tk, uint16_t* __restrict__ dW, float* __restrict__ w_soft_dbg) {
     constexpr int L = GridT<GRID>::L;
-    const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
+    constexpr int N = GridT<GRID>::N;
+    const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x) * N;
     if (i0 >= mk) return;
     const Idx<O32> ix{i0};
-    float l[L][4];
+    float l[L][N];
 #pragma unroll
-    for (int k = 0; k < L; ++k) load4(ix.at(logits, mk, k), l[k]);
-    float w[4];
-    load_w4(W, WBF16, ix, w);
+    for (int k = 0; k < L; ++k) loadv<N>(ix.at(logits, mk, k), l[k]);
+    float w[N];
+    load_w<N>(W, WBF16, ix, w);
     const float s = scales[i0 >> 7];
     uint32_t cw = 0;
-    if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = *reinterpret_cast<const uint32_t*>(ix.at(codes));
-    NoiseStream4<L> ns(i0, step, sid, key);
-    float out[4];
-    for4([&](auto cc) {
+    if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = load_codes<N>(codes, ix);
+    NoiseStream<L, N> ns(i0, step, sid, key);
+    float out[N];
+    forN<N>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
         uint32_t nz[L];
         ns.template words<c>(nz);
@@ -164,11 +240,8 @@ __global__ __launch_bounds__(kThreads) void relax_fwd_kernel(
         relax_coord<GRID>(lc, nz, static_cast<int>((cw >> (8 * c)) & 0xFF), tk, r);
         out[c] = s * r.what;
     });
-    if constexpr (DBG) store4(ix.at(w_soft_dbg), out);
-    uint2 o;
-    o.x = pack_bf16x2(out[0] - w[0], out[1] - w[1]);
-    o.y = pack_bf16x2(out[2] - w[2], out[3] - w[3]);
-    *reinterpret_cast<uint2*>(ix.at(dW)) = o;
+    if constexpr (DBG) storev<N>(ix.at(w_soft_dbg), out);
+    store_dw<N>(dW, ix, out, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -185,30 +258,32 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
     float* __restrict__ gl_dbg, float* __restrict__ gs_dbg, const void* __restrict__ W,
     uint32_t next_step, TauK tk_next, uint16_t* __restrict__ dW) {
     constexpr int L = GridT<GRID>::L;
-    const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
-    // Whole scale groups (32 threads) are either in range or not, so the
+    constexpr int N = GridT<GRID>::N;
+    constexpr int P = 128 / N;   // lanes per scale group
+    const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x) * N;
+    // Whole scale groups (P threads) are either in range or not, so the
     // shuffles below never read a lane that returned here.
     if (i0 >= mk) return;
     const Idx<O32> ix{i0};
-    float g[4];
-    load4(ix.at(G), g);
-    float l[L][4], m[L][4];
+    float g[N];
+    loadv<N>(ix.at(G), g);
+    float l[L][N], m[L][N];
 #pragma unroll
     for (int k = 0; k < L; ++k) {
-        load4(ix.at(logits, mk, k), l[k]);
-        load4(ix.at(mom, mk, k), m[k]);
+        loadv<N>(ix.at(logits, mk, k), l[k]);
+        loadv<N>(ix.at(mom, mk, k), m[k]);
     }
     const uint64_t grp = i0 >> 7;
     const float s = scales[grp];
     uint32_t cw = 0;
-    if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = *reinterpret_cast<const uint32_t*>(ix.at(codes));
+    if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = load_codes<N>(codes, ix);
     float gsum = 0.0f;
     {
-        NoiseStream4<L> ns(i0, step, sid, key);
+        NoiseStream<L, N> ns(i0, step, sid, key);
         const float gs_tau = s * tk.invtau;
         // Each coordinate's gradient goes straight into its Lion update, so
         // no gradient array stays live (fewer registers, more waves in flight).
-        for4([&](auto cc) {
+        forN<N>([&](auto cc) {
             constexpr int c = decltype(cc)::value;
             uint32_t nz[L];
             ns.template words<c>(nz);
@@ -237,27 +312,27 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
         });
 #pragma unroll
         for (int k = 0; k < L; ++k) {
-            store4(ix.at(logits, mk, k), l[k]);
-            store4(ix.at(mom, mk, k), m[k]);
+            storev<N>(ix.at(logits, mk, k), l[k]);
+            storev<N>(ix.at(mom, mk, k), m[k]);
         }
     }
     // Group sum, taken from the group's first lane so that every lane applies
     // the same Lion update to the shared scale.
-    gsum = __shfl(group32_sum(gsum), threadIdx.x & 32, 64);
+    gsum = __shfl(group_sum<P>(gsum), group_lane0<P>(), 64);
     float sn = s, smn = scale_mom[grp];
     lion_update(sn, smn, gsum, lks);
-    if ((threadIdx.x & 31) == 0) {
+    if ((threadIdx.x & (P - 1)) == 0) {
         scales[grp] = sn;
         scale_mom[grp] = smn;
         if constexpr (DBG) gs_dbg[grp] = gsum;
     }
     if constexpr (FWD_NEXT) {
         // W is only needed here; its load overlaps the next-step noise.
-        float w[4];
-        load_w4(W, WBF16, ix, w);
-        NoiseStream4<L> ns(i0, next_step, sid, key);
-        float out[4];
-        for4([&](auto cc) {
+        float w[N];
+        load_w<N>(W, WBF16, ix, w);
+        NoiseStream<L, N> ns(i0, next_step, sid, key);
+        float out[N];
+        forN<N>([&](auto cc) {
             constexpr int c = decltype(cc)::value;
             uint32_t nz[L];
             ns.template words<c>(nz);
@@ -268,10 +343,7 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
             relax_coord<GRID>(lc, nz, static_cast<int>((cw >> (8 * c)) & 0xFF), tk_next, r);
             out[c] = sn * r.what;
         });
-        uint2 o;
-        o.x = pack_bf16x2(out[0] - w[0], out[1] - w[1]);
-        o.y = pack_bf16x2(out[2] - w[2], out[3] - w[3]);
-        *reinterpret_cast<uint2*>(ix.at(dW)) = o;
+        store_dw<N>(dW, ix, out, w);
     }
 }
 
@@ -290,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void init_rtn_kernel(const void* __restri
     float w[4];
     load_w4(W, WBF16, Idx<false>{i0}, w);
     float amax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
-    amax = group32_max(amax);
+    amax = group_max<32>(amax);
     const float s = __fdiv_rn(amax, qmax);
     uint32_t cw = 0;
     float lg[L][4];
@@ -433,10 +505,19 @@ hipError_t launch_init_rtn(const LayerDesc& d, const void* W, float* scales, uin
 // plane does.
 inline bool off32(const LayerDesc& d) { return d.mk * 4 <= 0xFFFFFFF0ull; }
 
+// Threads of the relax kernels: one per N coordinates.
+inline uint64_t relax_threads(const LayerDesc& d) {
+    switch (d.grid) {
+        case GSQ_GRID_INT2: return d.mk / GridT<GSQ_GRID_INT2>::N;
+        case GSQ_GRID_TERNARY: return d.mk / GridT<GSQ_GRID_TERNARY>::N;
+        default: return d.mk / GridT<GSQ_GRID_INT3_LOCAL>::N;
+    }
+}
+
 hipError_t launch_relax_fwd(const LayerDesc& d, const float* logits, const float* scales,
                             const uint8_t* codes, const void* W, uint32_t step, TauK tk,
                             uint16_t* dW, float* w_soft_dbg, hipStream_t st) {
-    const unsigned nb = blocks_for(d.mk / 4);
+    const unsigned nb = blocks_for(relax_threads(d));
     const bool o32 = off32(d);
 #define GSQ_FWD(G, WB, DB, O) \
     GSQ_LAUNCH((relax_fwd_kernel<G, WB, DB, O>), nb, st, logits, scales, codes, W, d.mk, step, d.sid, d.key, tk, dW, w_soft_dbg)
@@ -463,7 +544,7 @@ hipError_t launch_relax_bwd_lion(const LayerDesc& d, const float* G, float* logi
                                  uint32_t step, TauK tk, LionK lkl, LionK lks,
                                  float* gl_dbg, float* gs_dbg, const void* W, uint32_t next_step,
                                  TauK tk_next, uint16_t* dW, hipStream_t st) {
-    const unsigned nb = blocks_for(d.mk / 4);
+    const unsigned nb = blocks_for(relax_threads(d));
     const bool dbg = gl_dbg != nullptr || gs_dbg != nullptr;
     const bool fwd = dW != nullptr;
     const bool o32 = off32(d);
