@@ -316,6 +316,32 @@ def recon_loss_grad_grouped(X_cat, tok_offsets, dW_cat, rows_per_expert: int):
     return RTs, loss, G
 
 
+def gram(X, bf16: bool = False) -> np.ndarray:
+    """Gram matrix H = X^T X of the calibration tokens ([in, in], fp64).
+
+    The reconstruction objective is a quadratic form in dW: ||X dW^T||_F^2 =
+    tr(dW X^T X dW^T), so H holds everything the objective needs from X
+    (agihunt.info, method paragraph: the objective is the output
+    reconstruction error). With ``bf16`` the result is rounded to bfloat16, as
+    the GPU stores it.
+    """
+    Xd = np.asarray(X, dtype=np.float64)
+    H = Xd.T @ Xd
+    return round_bf16(H).astype(np.float64) if bf16 else H
+
+
+def recon_loss_grad_gram(dW, H):
+    """The reconstruction objective and its gradient in Gram form.
+
+    With P = dW H: loss = sum(dW * P) = tr(dW H dW^T) and G = 2 P, equal to
+    :func:`recon_loss_grad` when H = X^T X. One product of 2*out*in*in flops
+    instead of two of 2*out*tokens*in. Returns ``(loss, G)``.
+    """
+    D = np.asarray(dW, dtype=np.float64)
+    P = D @ np.asarray(H, dtype=np.float64)
+    return float(np.sum(D * P)), 2.0 * P
+
+
 def hard_loss(codes, scales, W, X, grid: int, group: int = 128) -> float:
     """Reconstruction error of a hard assignment: ||X (s*v(codes) - W)^T||^2.
 

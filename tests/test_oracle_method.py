@@ -222,6 +222,63 @@ def test_loss_and_gradient_gram_form():
         assert abs(fd - G[idx]) <= 1e-6 * np.abs(G).max()
 
 
+def test_gram_matrix_by_token_sums():
+    # H[i][j] = sum over tokens of x_i * x_j, accumulated one token at a time.
+    rng = np.random.default_rng(5)
+    X = rng.normal(size=(9, 6))
+    H = oracle.gram(X)
+    want = np.zeros((6, 6))
+    for n in range(9):
+        for i in range(6):
+            for j in range(6):
+                want[i, j] += X[n, i] * X[n, j]
+    np.testing.assert_allclose(H, want, rtol=1e-13, atol=1e-13)
+    assert np.array_equal(H, H.T)
+    assert np.linalg.eigvalsh(H).min() >= -1e-12
+
+
+def test_gram_bf16_is_rounded_exact_gram():
+    rng = np.random.default_rng(6)
+    X = rng.normal(size=(64, 32)) * 3.0
+    Hb = oracle.gram(X, bf16=True)
+    He = oracle.gram(X)
+    # every entry is a bf16 value (low 16 bits of the fp32 pattern are zero)
+    assert not (Hb.astype(np.float32).view(np.uint32) & 0xFFFF).any()
+    # and within half a bf16 ulp (2^-8 relative) of the exact value
+    assert np.all(np.abs(Hb - He) <= np.abs(He) * 2.0 ** -8 + 1e-30)
+
+
+def test_gram_objective_equals_direct_objective():
+    # Same objective written two ways: tr(dW X^T X dW^T) and ||X dW^T||^2;
+    # the direct form is pinned by finite differences above.
+    rng = np.random.default_rng(7)
+    X = rng.normal(size=(50, 40))
+    D = rng.normal(size=(9, 40)) * 0.01
+    _, loss, G = oracle.recon_loss_grad(X, D)
+    lg, Gg = oracle.recon_loss_grad_gram(D, oracle.gram(X))
+    assert math.isclose(lg, loss, rel_tol=1e-12)
+    np.testing.assert_allclose(Gg, G, rtol=1e-11, atol=1e-15)
+    # a single nonzero row r: the loss is the quadratic form d_r H d_r^T
+    D1 = np.zeros_like(D)
+    D1[4] = D[4]
+    l1, _ = oracle.recon_loss_grad_gram(D1, oracle.gram(X))
+    assert math.isclose(l1, float(np.sum((X @ D[4]) ** 2)), rel_tol=1e-12)
+
+
+def test_gram_gradient_finite_differences():
+    rng = np.random.default_rng(8)
+    H = oracle.gram(rng.normal(size=(30, 12)))
+    D = rng.normal(size=(4, 12)) * 0.1
+    _, G = oracle.recon_loss_grad_gram(D, H)
+    h = 1e-6
+    for idx in [(0, 0), (2, 7), (3, 11)]:
+        Dp, Dm = D.copy(), D.copy()
+        Dp[idx] += h
+        Dm[idx] -= h
+        fd = (oracle.recon_loss_grad_gram(Dp, H)[0] - oracle.recon_loss_grad_gram(Dm, H)[0]) / (2 * h)
+        assert abs(fd - G[idx]) <= 1e-7 * np.abs(G).max()
+
+
 def test_zero_difference_gives_zero_loss_and_gradient():
     X = np.random.default_rng(0).normal(size=(8, 16))
     RT, loss, G = oracle.recon_loss_grad(X, np.zeros((3, 16)))
