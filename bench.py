@@ -87,6 +87,33 @@ def cpu_baseline(data, rows: int):
                       f"NumPy elementwise work on one thread, BLAS on {blas_threads}"}
 
 
+def time_fused(solver, taus, warmup: int, steps: int, stream):
+    """Fused-step timing loop: returns (elapsed s, mean recon ms, mean fused
+    backward+forward ms). Step t = objective of step t (dW from the previous
+    pass) + backward and Lion of step t fused with the forward of step t + 1."""
+    import numpy as np
+    import torch
+    solver.relax_fwd(0, taus[0])
+    for t in range(warmup):
+        solver.step_fused(t, taus[t], taus[t + 1])
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        t = warmup + i
+        e = ev[i]
+        e[0].record(stream)
+        solver.recon()
+        e[1].record(stream)
+        solver.relax_bwd_lion_fwd(t, taus[t], t + 1, taus[t + 1])
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    rec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    fus_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    return elapsed, rec_ms, fus_ms
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +123,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--unfused", action="store_true",
                     help="time separate forward and backward calls instead of the fused pass")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the Gram-form variant measured after the headline step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the step shards by output rows with no "
@@ -161,26 +190,7 @@ def main():
         per_launch = {"relax_fwd": fwd_ms, "recon_loss_grad": rec_ms / 2, "relax_bwd_lion": bwd_ms}
         bytes_per = {"relax_fwd": FWD_BYTES_PER_COORD, "relax_bwd_lion": BWD_BYTES_PER_COORD}
     else:
-        # Step t = objective of step t (dW from the previous pass) + backward
-        # and Lion of step t fused with the forward of step t + 1.
-        solver.relax_fwd(0, taus[0])
-        for t in range(args.warmup):
-            solver.step_fused(t, taus[t], taus[t + 1])
-        torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            t = args.warmup + i
-            e = ev[i]
-            e[0].record(stream)
-            solver.recon()
-            e[1].record(stream)
-            solver.relax_bwd_lion_fwd(t, taus[t], t + 1, taus[t + 1])
-            e[2].record(stream)
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-        rec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-        fus_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        elapsed, rec_ms, fus_ms = time_fused(solver, taus, args.warmup, args.steps, stream)
         kernels = {
             "recon_loss_grad": {"ms": rec_ms, "TFLOP/s": gemm_flops / rec_ms / 1e9,
                                 "note": "two bf16 GEMMs (2NMK flops each) + loss finalize"},
@@ -230,6 +240,27 @@ def main():
         "kernels": kernels,
         "last_loss": loss,
     }
+    if not args.no_variants and not args.unfused:
+        # Same step with the objective in Gram form (H = X^T X formed once,
+        # untimed; one product of 2*M*K*K flops per step instead of two of
+        # 2*N*M*K), on a fresh solver. Reported beside the headline, which
+        # keeps the two-product form.
+        del solver
+        torch.cuda.empty_cache()
+        gsol = LayerSolver(Wd, Xd, g.GRID_INT2, seed=0, stream_id=0, recon="gram",
+                           lion=g.GsqLion.make(lr_logit=wl.lr_logit, lr_scale=1e-5))
+        g_el, g_rec, g_fus = time_fused(gsol, taus, args.warmup, args.steps, stream)
+        gram_flops = 2.0 * M * K * K
+        out["variants"] = {"gram": {
+            "value": coords * args.steps / g_el, "unit": "weights/s",
+            "ms_per_step": g_el * 1e3 / args.steps,
+            "recon_gram": {"ms": g_rec, "TFLOP/s": gram_flops / g_rec / 1e9,
+                           "note": "one bf16 GEMM dW H (2MK^2 flops) + loss finalize"},
+            "relax_bwd_lion_fwd": {"ms": g_fus,
+                                   "GB/s": FUSED_BYTES_PER_COORD * coords / g_fus / 1e6},
+            "last_loss": float(gsol.loss.item()),
+        }}
+        del gsol
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(data, args.cpu_rows)
     print(json.dumps(out), flush=True)

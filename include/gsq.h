@@ -185,6 +185,37 @@ gsq_status gsq_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets,
                                 int64_t cols, const uint16_t* X, uint16_t* XT,
                                 void* stream);
 
+/* Gram form of the same objective, for one dense layer. The reconstruction
+ * error is a quadratic form in dW, ||X dW^T||^2 = tr(dW H dW^T) with
+ * H = X^T X (agihunt.info method paragraph: the objective is the output
+ * reconstruction error), so H, formed once per layer, replaces X in every
+ * step: one product of 2*rows*cols^2 flops instead of two of
+ * 2*rows*tokens*cols, fewer when cols < 2*tokens.
+ *
+ * gsq_gram: H = X^T X, fp32 accumulation, rounded to bf16 (nearest even).
+ *   tokens  T, a multiple of 64 (zero rows pad it)
+ *   cols    in features (multiple of 128)
+ *   XT      [cols][T] bf16 (gsq_transpose_tokens with one expert)
+ *   H       out [cols][cols] bf16 (symmetric) */
+gsq_status gsq_gram(int64_t tokens, int64_t cols, const uint16_t* XT, uint16_t* H,
+                    void* stream);
+
+/* Workspace bytes gsq_recon_gram needs (loss partials). */
+size_t gsq_recon_gram_workspace_bytes(int64_t rows, int64_t cols);
+
+/* P = dW H (bf16 operands, fp32 accumulation), G = 2 P, loss = sum dW * P
+ * (equal to gsq_recon_loss_grad's loss and G up to rounding, with the bf16
+ * rounding of H in place of that of R).
+ *   H          [cols][cols] bf16 from gsq_gram
+ *   dW_bf16    [rows][cols] bf16
+ *   workspace  device scratch of at least gsq_recon_gram_workspace_bytes()
+ *   G          out [rows][cols] fp32
+ *   loss       out device scalar, fp64 (deterministic fixed-order sum) */
+gsq_status gsq_recon_gram(int64_t rows, int64_t cols, const uint16_t* H,
+                          const uint16_t* dW_bf16, void* workspace,
+                          size_t workspace_bytes, float* G, double* loss,
+                          void* stream);
+
 /* Relaxed backward and Lion, in place (agihunt.info method and optimizer
  * paragraphs). Regenerates the step's noise (same `step`, `tau` and
  * `noise_scale` as the forward) and, with G = dLoss/dW_soft:

@@ -481,7 +481,7 @@ def step(state: dict, W, X, grid: int, t: int, tau: float, seed: int,
          stream: int, lr_logit: float, lr_scale: float, beta1: float = 0.9,
          beta2: float = 0.99, weight_decay: float = 0.0,
          noise_scale: float = 1.0, bf16_dW: bool = False, group: int = 128,
-         bf16_RT: bool = False):
+         bf16_RT: bool = False, H=None):
     """One full relaxed-quantization step on a whole layer, in place on
     ``state`` (``logits``, ``mom``, ``scales``, ``scale_mom``, ``codes``).
 
@@ -489,15 +489,19 @@ def step(state: dict, W, X, grid: int, t: int, tau: float, seed: int,
     logits and scales, Lion on both. ``bf16_dW`` rounds dW to bfloat16 before
     the products and ``bf16_RT`` rounds R^T to bfloat16 before forming G, as
     a bf16 matrix engine consumes them (the loss stays the exact sum of R^2).
-    Returns the loss.
+    With a Gram matrix ``H`` (see :func:`gram`) the objective is taken in Gram
+    form instead and X is not used. Returns the loss.
     """
     codes = state["codes"] if grid == GRID_INT3_LOCAL else None
     f = relax_fwd(state["logits"], state["scales"], W, grid, seed, stream, t,
                   tau, noise_scale, codes, 0, group)
     dW = round_bf16(f["dW"]).astype(np.float64) if bf16_dW else f["dW"]
-    RT, loss, G = recon_loss_grad(X, dW)
-    if bf16_RT:
-        G = 2.0 * (round_bf16(RT).astype(np.float64) @ np.asarray(X, dtype=np.float64))
+    if H is not None:
+        loss, G = recon_loss_grad_gram(dW, H)
+    else:
+        RT, loss, G = recon_loss_grad(X, dW)
+        if bf16_RT:
+            G = 2.0 * (round_bf16(RT).astype(np.float64) @ np.asarray(X, dtype=np.float64))
     gl, gs = relax_bwd(G, state["logits"], state["scales"], grid, seed, stream,
                        t, tau, noise_scale, codes, 0, group)
     state["logits"], state["mom"] = lion(state["logits"], gl, state["mom"],

@@ -18,8 +18,8 @@ __all__ = [
     "GsqError", "GsqLayer", "GsqLion", "lib", "exported_symbols",
     "gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
     "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
-    "gsq_transpose_tokens", "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd", "gsq_harden_pack",
-    "gsq_noise_dump",
+    "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes", "gsq_recon_gram",
+    "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd", "gsq_harden_pack", "gsq_noise_dump",
 ]
 
 GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL = 0, 1, 2
@@ -32,7 +32,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsq.so")
 #: Entry points declared in include/gsq.h.
 EXPORTS = ("gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
            "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
-           "gsq_transpose_tokens", "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd",
+           "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes",
+           "gsq_recon_gram", "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd",
            "gsq_harden_pack", "gsq_noise_dump")
 
 
@@ -95,6 +96,10 @@ def lib() -> ctypes.CDLL:
         "gsq_recon_loss_grad": (st, [ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                      _P, _P, ctypes.c_size_t, _P, _P, _P, _P]),
         "gsq_transpose_tokens": (st, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
+        "gsq_gram": (st, [ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
+        "gsq_recon_gram_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
+        "gsq_recon_gram": (st, [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t, _P, _P,
+                                _P]),
         "gsq_relax_bwd_lion": (st, [_L, _P, _P, _P, _P, _P, _P, ctypes.c_uint32, ctypes.c_float,
                                     ctypes.c_float, ctypes.POINTER(GsqLion), _P, _P, _P]),
         "gsq_relax_bwd_lion_fwd": (st, [_L, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32,
@@ -200,6 +205,23 @@ def gsq_transpose_tokens(n_experts: int, tok_offsets, cols: int, X, XT, stream=N
     arr, p = _offsets(tok_offsets)
     _check("gsq_transpose_tokens", lib().gsq_transpose_tokens(n_experts, p, cols, _ptr(X),
                                                               _ptr(XT), _stream(stream)))
+
+
+def gsq_gram(tokens: int, cols: int, XT, H, stream=None):
+    _check("gsq_gram", lib().gsq_gram(tokens, cols, _ptr(XT), _ptr(H), _stream(stream)))
+
+
+def gsq_recon_gram_workspace_bytes(rows: int, cols: int) -> int:
+    return lib().gsq_recon_gram_workspace_bytes(rows, cols)
+
+
+def gsq_recon_gram(rows: int, cols: int, H, dW_bf16, workspace, G, loss, stream=None,
+                   workspace_bytes=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("gsq_recon_gram",
+           lib().gsq_recon_gram(rows, cols, _ptr(H), _ptr(dW_bf16), _ptr(workspace),
+                                workspace_bytes, _ptr(G), _ptr(loss), _stream(stream)))
 
 
 def gsq_relax_bwd_lion(layer: GsqLayer, G, logits, mom, scales, scale_mom, init_codes,

@@ -193,6 +193,48 @@ gsq_status gsq_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets, i
                                                    static_cast<hipStream_t>(stream)));
 }
 
+// The GEMM addresses each bf16 operand with 32-bit byte offsets below 2^31
+// (plus the contraction length), so an operand must stay under about 2 GiB.
+inline bool gemm_operand_fits(int64_t rows, int64_t ld, int64_t contraction) {
+    return rows * ld * 2 <= int64_t(0x7FFFFF00) - 2 * contraction;
+}
+
+gsq_status gsq_gram(int64_t tokens, int64_t cols, const uint16_t* XT, uint16_t* H, void* stream) {
+    if (tokens <= 0 || (tokens % 64) != 0 || tokens > INT32_MAX) return GSQ_ERR_SHAPE;
+    if (cols <= 0 || (cols % 128) != 0 || cols > INT32_MAX) return GSQ_ERR_SHAPE;
+    if (tokens > kMaxCoords / cols || cols > kMaxCoords / cols) return GSQ_ERR_SHAPE;
+    if (!gemm_operand_fits(cols, tokens, tokens)) return GSQ_ERR_SHAPE;
+    GSQ_TRY(need(XT));
+    GSQ_TRY(need(H));
+    return hip_status(gsq::launch_gram(tokens, cols, XT, H, static_cast<hipStream_t>(stream)));
+}
+
+size_t gsq_recon_gram_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || rows > INT32_MAX || cols <= 0 || (cols % 128) != 0 || cols > INT32_MAX)
+        return 0;
+    const size_t n = gsq::gram_partials(rows, cols);
+    return ((n * sizeof(float) + 255) / 256) * 256 + 256;
+}
+
+gsq_status gsq_recon_gram(int64_t rows, int64_t cols, const uint16_t* H, const uint16_t* dW_bf16,
+                          void* workspace, size_t workspace_bytes, float* G, double* loss,
+                          void* stream) {
+    if (rows <= 0 || rows > INT32_MAX) return GSQ_ERR_SHAPE;
+    if (cols <= 0 || (cols % 128) != 0 || cols > INT32_MAX) return GSQ_ERR_SHAPE;
+    if (rows > kMaxCoords / cols || cols > kMaxCoords / cols) return GSQ_ERR_SHAPE;
+    if (!gemm_operand_fits(rows, cols, cols) || !gemm_operand_fits(cols, cols, cols))
+        return GSQ_ERR_SHAPE;
+    GSQ_TRY(need(H));
+    GSQ_TRY(need(dW_bf16));
+    GSQ_TRY(need(workspace));
+    GSQ_TRY(need(G));
+    GSQ_TRY(need(loss));
+    if (workspace_bytes < gsq_recon_gram_workspace_bytes(rows, cols)) return GSQ_ERR_SHAPE;
+    return hip_status(gsq::launch_recon_gram(rows, cols, H, dW_bf16,
+                                             static_cast<float*>(workspace), G, loss,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 gsq_status gsq_relax_bwd_lion(const gsq_layer* layer, const float* G, float* logits, float* mom,
                               float* scales, float* scale_mom, const uint8_t* init_codes,
                               uint32_t step, float tau, float noise_scale, const gsq_lion* lion,

@@ -36,7 +36,11 @@ constexpr uint32_t kOob = 0x7FFFFF00u;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-enum { EPI_BF16_LOSS = 0, EPI_F32_SCALED = 1 };
+// Epilogues: bf16 output plus the tile's sum of squares (GEMM1); fp32 output
+// times alpha (GEMM2); plain bf16 output (the Gram matrix); fp32 output times
+// alpha plus the tile's sum of D[i][j] * C[i][j] before scaling (the Gram-form
+// step, where D = dW and C = dW H, so the sum is the loss).
+enum { EPI_BF16_LOSS = 0, EPI_F32_SCALED = 1, EPI_BF16 = 2, EPI_F32_GRAM = 3 };
 
 struct GemmArgs {
     const uint16_t* A;
@@ -47,7 +51,9 @@ struct GemmArgs {
     int tiles_i, tiles_j;
     void* C;
     float alpha;
-    float* partials;   // EPI_BF16_LOSS: one float per workgroup
+    float* partials;   // EPI_BF16_LOSS, EPI_F32_GRAM: one float per workgroup
+    const uint16_t* D; // EPI_F32_GRAM: bf16 [I][ldd] paired with the output
+    int64_t ldd;
 };
 
 __device__ __forceinline__ void tile_of(const GemmArgs& g, int& ti, int& tj) {
@@ -284,7 +290,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
             }
         }
         __syncthreads();
-        if constexpr (EPI == EPI_BF16_LOSS) {
+        if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_BF16) {
             // 16 lanes per 128-value row: 8 values -> one 16-byte bf16 store.
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -295,10 +301,12 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
                 const int grow = grow0 + a * 32 + row, gcol = gcol0 + col;
                 if (grow < g.I && gcol < g.J) {
                     const int64_t off = static_cast<int64_t>(grow) * g.ldc + gcol;
-                    lsum = __builtin_fmaf(v0.x, v0.x, lsum); lsum = __builtin_fmaf(v0.y, v0.y, lsum);
-                    lsum = __builtin_fmaf(v0.z, v0.z, lsum); lsum = __builtin_fmaf(v0.w, v0.w, lsum);
-                    lsum = __builtin_fmaf(v1.x, v1.x, lsum); lsum = __builtin_fmaf(v1.y, v1.y, lsum);
-                    lsum = __builtin_fmaf(v1.z, v1.z, lsum); lsum = __builtin_fmaf(v1.w, v1.w, lsum);
+                    if constexpr (EPI == EPI_BF16_LOSS) {
+                        lsum = __builtin_fmaf(v0.x, v0.x, lsum); lsum = __builtin_fmaf(v0.y, v0.y, lsum);
+                        lsum = __builtin_fmaf(v0.z, v0.z, lsum); lsum = __builtin_fmaf(v0.w, v0.w, lsum);
+                        lsum = __builtin_fmaf(v1.x, v1.x, lsum); lsum = __builtin_fmaf(v1.y, v1.y, lsum);
+                        lsum = __builtin_fmaf(v1.z, v1.z, lsum); lsum = __builtin_fmaf(v1.w, v1.w, lsum);
+                    }
                     uint4 o;
                     o.x = pack_bf16x2(v0.x, v0.y); o.y = pack_bf16x2(v0.z, v0.w);
                     o.z = pack_bf16x2(v1.x, v1.y); o.w = pack_bf16x2(v1.z, v1.w);
@@ -316,6 +324,14 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
                 const int grow = grow0 + a * 32 + row, gcol = gcol0 + col;
                 if (grow < g.I && gcol < g.J) {
                     const int64_t off = static_cast<int64_t>(grow) * g.ldc + gcol;
+                    if constexpr (EPI == EPI_F32_GRAM) {
+                        const uint2 d = *reinterpret_cast<const uint2*>(
+                            g.D + static_cast<int64_t>(grow) * g.ldd + gcol);
+                        lsum = __builtin_fmaf(bf16_lo(d.x), v.x, lsum);
+                        lsum = __builtin_fmaf(bf16_hi(d.x), v.y, lsum);
+                        lsum = __builtin_fmaf(bf16_lo(d.y), v.z, lsum);
+                        lsum = __builtin_fmaf(bf16_hi(d.y), v.w, lsum);
+                    }
                     *reinterpret_cast<float4*>(static_cast<float*>(g.C) + off) =
                         make_float4(g.alpha * v.x, g.alpha * v.y, g.alpha * v.z, g.alpha * v.w);
                 }
@@ -323,7 +339,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
         }
         __syncthreads();
     }
-    if constexpr (EPI == EPI_BF16_LOSS) {
+    if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_F32_GRAM) {
         // Fixed-order reduction: wave butterfly, then waves 0..3 in order.
         __shared__ float red[NT / 64];
 #pragma unroll
@@ -371,8 +387,10 @@ inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b)
 
 template <int EPI>
 hipError_t run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int I, int J,
-                    int Rd, void* C, int64_t ldc, float alpha, float* partials, hipStream_t st) {
+                    int Rd, void* C, int64_t ldc, float alpha, float* partials, hipStream_t st,
+                    const uint16_t* D = nullptr, int64_t ldd = 0) {
     GemmArgs g;
+    g.D = D; g.ldd = ldd;
     g.A = A; g.B = B; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
     g.I = I; g.J = J; g.Rd = Rd;
     const int64_t ab = static_cast<int64_t>(I) * lda * 2, bb = static_cast<int64_t>(J) * ldb * 2;
@@ -430,6 +448,29 @@ hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t r
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(256), 0, st, partials,
                        static_cast<int>(slot), loss);
+    return hipGetLastError();
+}
+
+size_t gram_partials(int64_t rows, int64_t cols) {
+    return static_cast<size_t>(cdiv(rows, BM)) * cdiv(cols, BN);
+}
+
+hipError_t launch_gram(int64_t tokens, int64_t cols, const uint16_t* XT, uint16_t* H,
+                       hipStream_t st) {
+    // H[i][j] = sum_n XT[i][n] XT[j][n]: an NT product of X^T with itself.
+    return run_gemm<EPI_BF16>(XT, tokens, XT, tokens, static_cast<int>(cols), static_cast<int>(cols),
+                              static_cast<int>(tokens), H, cols, 1.0f, nullptr, st);
+}
+
+hipError_t launch_recon_gram(int64_t rows, int64_t cols, const uint16_t* H, const uint16_t* dW,
+                             float* partials, float* G, double* loss, hipStream_t st) {
+    // C = dW H^T = dW H (H is symmetric); G = 2 C; loss = sum dW * C.
+    hipError_t err = run_gemm<EPI_F32_GRAM>(dW, cols, H, cols, static_cast<int>(rows),
+                                            static_cast<int>(cols), static_cast<int>(cols), G, cols,
+                                            2.0f, partials, st, dW, cols);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(256), 0, st, partials,
+                       static_cast<int>(gram_partials(rows, cols)), loss);
     return hipGetLastError();
 }
 

@@ -49,6 +49,11 @@ size_t recon_partials(int32_t n_experts, const int64_t* tok_offsets, int64_t row
 hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t rows_per_expert,
                         int64_t cols, const uint16_t* X, const uint16_t* XT, const uint16_t* dW,
                         float* partials, uint16_t* RT, float* G, double* loss, hipStream_t st);
+size_t gram_partials(int64_t rows, int64_t cols);
+hipError_t launch_gram(int64_t tokens, int64_t cols, const uint16_t* XT, uint16_t* H,
+                       hipStream_t st);
+hipError_t launch_recon_gram(int64_t rows, int64_t cols, const uint16_t* H, const uint16_t* dW,
+                             float* partials, float* G, double* loss, hipStream_t st);
 hipError_t launch_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets, int64_t cols,
                                    const uint16_t* X, uint16_t* XT, hipStream_t st);
 

@@ -8,7 +8,9 @@ state of one layer (or one batch of experts) for the whole annealed solve:
 * group scales and their momentum, [rows][cols/128] fp32;
 * warm-start codes, [rows][cols] uint8;
 * dW (bf16), G (fp32), R^T (bf16) and the loss partial workspace;
-* the calibration tokens X (bf16) and their per-expert transpose X^T.
+* the calibration tokens X (bf16) and their per-expert transpose X^T;
+* with ``recon="gram"`` (one dense layer): H = X^T X (bf16, [in][in]) in
+  place of R^T, so each step runs one product dW H instead of two.
 
 Memory per coordinate: 8L bytes of logits + momentum, 1 (codes), 2 (dW),
 4 (G), plus W itself; R^T, X and X^T scale with the token count.
@@ -23,7 +25,8 @@ import torch
 
 from . import (GRID_INT3_LOCAL, DTYPE_BF16, DTYPE_F32, N_LOGITS, CODE_BITS, GsqLayer,
                GsqLion, gsq_init_rtn, gsq_relax_fwd, gsq_recon_workspace_bytes,
-               gsq_recon_loss_grad, gsq_transpose_tokens, gsq_relax_bwd_lion,
+               gsq_recon_loss_grad, gsq_transpose_tokens, gsq_gram,
+               gsq_recon_gram_workspace_bytes, gsq_recon_gram, gsq_relax_bwd_lion,
                gsq_relax_bwd_lion_fwd, gsq_harden_pack)
 
 TOKEN_ALIGN = 64
@@ -59,7 +62,8 @@ class LayerSolver:
 
     def __init__(self, W: torch.Tensor, X: torch.Tensor, grid: int, tok_offsets=None,
                  rows_per_expert: int | None = None, seed: int = 0, stream_id: int = 0,
-                 lion: GsqLion | None = None, init_logit: float = 2.0):
+                 lion: GsqLion | None = None, init_logit: float = 2.0,
+                 recon: str = "direct"):
         if not (W.is_cuda and X.is_cuda):
             raise ValueError("W and X must be device tensors")
         if W.dtype not in (torch.bfloat16, torch.float32) or X.dtype != torch.bfloat16:
@@ -75,6 +79,11 @@ class LayerSolver:
         self.rows_per_expert = rows_per_expert or self.rows // self.n_experts
         if self.rows_per_expert * self.n_experts != self.rows:
             raise ValueError("rows must equal n_experts * rows_per_expert")
+        if recon not in ("direct", "gram"):
+            raise ValueError("recon must be 'direct' or 'gram'")
+        if recon == "gram" and self.n_experts != 1:
+            raise ValueError("the Gram form is for one dense layer (n_experts = 1)")
+        self.recon_mode = recon
         self.X, self.tok_offsets = pad_tokens(X, tok_offsets)
         self.tokens = int(self.tok_offsets[-1])
         self.layer = GsqLayer.make(grid, self.rows, self.cols,
@@ -90,14 +99,25 @@ class LayerSolver:
         self.codes = torch.empty((M, K), dtype=torch.uint8, device=dev)
         self.dW = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         self.G = torch.empty((M, K), **f32)
-        self.RT = torch.empty((max(1, self.rows_per_expert * self.tokens),), dtype=torch.bfloat16,
-                              device=dev)
         self.XT = torch.empty((max(1, self.tokens * K),), dtype=torch.bfloat16, device=dev)
-        ws = gsq_recon_workspace_bytes(self.n_experts, self.tok_offsets, self.rows_per_expert, K)
+        if recon == "gram":
+            self.RT = None
+            self.H = torch.empty((K, K), dtype=torch.bfloat16, device=dev)
+            ws = gsq_recon_gram_workspace_bytes(M, K)
+        else:
+            self.RT = torch.empty((max(1, self.rows_per_expert * self.tokens),),
+                                  dtype=torch.bfloat16, device=dev)
+            self.H = None
+            ws = gsq_recon_workspace_bytes(self.n_experts, self.tok_offsets, self.rows_per_expert, K)
         self.workspace = torch.empty((max(ws, 256) // 4,), **f32)
         self.loss = torch.zeros((1,), dtype=torch.float64, device=dev)
         gsq_init_rtn(self.layer, self.W, self.scales, self.codes, self.logits, init_logit)
         gsq_transpose_tokens(self.n_experts, self.tok_offsets, K, self.X, self.XT)
+        if recon == "gram":
+            if self.tokens == 0:
+                self.H.zero_()
+            else:
+                gsq_gram(self.tokens, K, self.XT, self.H)
 
     @property
     def init_codes(self):
@@ -108,8 +128,12 @@ class LayerSolver:
                       noise_scale, self.dW, w_soft_dbg)
 
     def recon(self):
-        gsq_recon_loss_grad(self.n_experts, self.tok_offsets, self.rows_per_expert, self.cols,
-                            self.X, self.XT, self.dW, self.workspace, self.RT, self.G, self.loss)
+        if self.recon_mode == "gram":
+            gsq_recon_gram(self.rows, self.cols, self.H, self.dW, self.workspace, self.G, self.loss)
+        else:
+            gsq_recon_loss_grad(self.n_experts, self.tok_offsets, self.rows_per_expert, self.cols,
+                                self.X, self.XT, self.dW, self.workspace, self.RT, self.G,
+                                self.loss)
 
     def relax_bwd_lion(self, step: int, tau: float, noise_scale: float = 1.0,
                        grad_logits_dbg=None, grad_scales_dbg=None):

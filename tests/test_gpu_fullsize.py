@@ -183,3 +183,52 @@ def test_step_is_deterministic():
         del sol
     for a, b in zip(*results):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["qproj4096_int2", "gateproj28672x8192_int3local"])
+def test_fullsize_gram(name):
+    """The Gram-form objective at full size: sampled rows of H = X^T X and of
+    G = 2 dW H from the GPU's own bf16 operands, and the loss against the
+    direct form's GPU loss on the same dW."""
+    import torch
+    from post_weight_quantization_philox_amd.solver import LayerSolver
+    dev = device()
+    d = synthetic.generate(name, seed=0)
+    wl = d["workload"]
+    Wd = to_dev_bf16(d["W_bits"], dev)
+    Xd = to_dev_bf16(d["X_bits"], dev)
+    X = d["X"].astype(np.float64)
+    N = X.shape[0]
+    sol = LayerSolver(Wd, Xd, wl.grid, seed=0, stream_id=0, recon="gram")
+    M, K = sol.rows, sol.cols
+    sol.relax_fwd(0, 0.5)
+    sol.recon()
+    torch.cuda.synchronize()
+    loss_gram = float(sol.loss.item())
+    rng = np.random.default_rng(1)
+    hrows = sorted({0, K - 1, *(int(r) for r in rng.integers(0, K, 6))})
+    H_rows = bf16_values(sol.H[hrows]).astype(np.float64)
+    for j, r in enumerate(hrows):
+        ref = X.T @ X[:, r]
+        gam = (N + 2) * 2.0 ** -24 * (np.abs(X).T @ np.abs(X[:, r]))
+        assert np.all(np.abs(H_rows[j] - ref) <= 0.5 * bf16_ulp(ref) + gam + 1e-30)
+    _log(f"{name}: gram rows {hrows} ok")
+    H = bf16_values(sol.H).astype(np.float64)
+    rows = _sample_rows(M, M)
+    dW_rows = bf16_values(sol.dW[rows]).astype(np.float64)
+    G_rows = f32(sol.G[rows]).astype(np.float64)
+    P = dW_rows @ H
+    bound = (K + 2) * 2.0 ** -24 * 2.0 * (np.abs(dW_rows) @ np.abs(H))
+    assert np.all(np.abs(G_rows - 2.0 * P) <= bound + 1e-30)
+    del H
+    _log(f"{name}: gram G rows {rows} ok")
+    # The direct form on the same dW (GPU): the two roundings of the same
+    # objective stay within 2e-3 of the exact value each.
+    dsol = LayerSolver(Wd, Xd, wl.grid, seed=0, stream_id=0)
+    dsol.dW.copy_(sol.dW)
+    dsol.recon()
+    torch.cuda.synchronize()
+    loss_direct = float(dsol.loss.item())
+    rel = abs(loss_gram - loss_direct) / loss_direct
+    report(f"{name} gram", loss_gram=loss_gram, loss_direct=loss_direct, rel=rel)
+    assert rel <= 4e-3

@@ -278,6 +278,73 @@ def test_recon_loss_grad(dev, M, N, K, offs):
         assert nrm <= 1e-5
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (512, 256, 512),                  # several tiles
+    (300, 192, 384),                  # ragged rows, partial tiles
+    (256, 64, 640),                   # few tokens, in-features past two tiles
+])
+def test_recon_gram(dev, M, N, K):
+    import torch
+    import post_weight_quantization_philox_amd as g
+    rng = np.random.default_rng(7 * M + N + K)
+    dW_bits = synthetic.bf16_bits((rng.normal(0, 0.01, (M, K))).astype(np.float32))
+    X_bits = synthetic.bf16_bits(rng.normal(0, 1, (N, K)).astype(np.float32))
+    dW = synthetic.bf16_to_f32(dW_bits).astype(np.float64)
+    X = synthetic.bf16_to_f32(X_bits).astype(np.float64)
+    tdW = to_dev_bf16(dW_bits, dev)
+    tX = to_dev_bf16(X_bits, dev)
+    XT = torch.empty((N * K,), dtype=torch.bfloat16, device=dev)
+    g.gsq_transpose_tokens(1, [0, N], K, tX, XT)
+    H = torch.empty((K, K), dtype=torch.bfloat16, device=dev)
+    g.gsq_gram(N, K, XT, H)
+    G = torch.full((M, K), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty((g.gsq_recon_gram_workspace_bytes(M, K) // 4,), dtype=torch.float32, device=dev)
+    loss = torch.zeros((1,), dtype=torch.float64, device=dev)
+    g.gsq_recon_gram(M, K, H, tdW, ws, G, loss)
+    torch.cuda.synchronize()
+    # H: an fp32 dot product of N terms rounded once to bf16.
+    Hh = bf16_values(H).astype(np.float64)
+    H_ref = oracle.gram(X)
+    gam = (N + 2) * 2.0 ** -24 * (np.abs(X).T @ np.abs(X))
+    assert np.all(np.abs(Hh - H_ref) <= 0.5 * bf16_ulp(H_ref) + gam + 1e-30)
+    report(f"gram {N}x{K}", asym=float(np.abs(Hh - Hh.T).max()))
+    # G and the loss from the GPU's own bf16 H, exact in fp64, against
+    # worst-case fp32 accumulation bounds (K terms per product, then at most
+    # 300 terms per fp32 partial of the loss).
+    l_ref, G_ref = oracle.recon_loss_grad_gram(dW, Hh)
+    Gd = f32(G).astype(np.float64)
+    bound = (K + 2) * 2.0 ** -24 * 2.0 * (np.abs(dW) @ np.abs(Hh))
+    assert np.all(np.abs(Gd - G_ref) <= bound + 1e-30)
+    lb = (K + 2) * 2.0 ** -24 * np.sum(np.abs(dW) * (np.abs(dW) @ np.abs(Hh))) \
+        + 300 * 2.0 ** -24 * np.sum(np.abs(dW * G_ref / 2))
+    got = float(loss.item())
+    assert abs(got - l_ref) <= lb
+    # Against the direct form's exact objective: the bf16 rounding of H moves
+    # the loss by far less than the 2e-3 allowed for a bf16-GEMM loss.
+    _, l_exact, G_exact = oracle.recon_loss_grad(X, dW)
+    rel = abs(got - l_exact) / l_exact
+    nrm = np.linalg.norm(Gd - G_exact) / np.linalg.norm(G_exact)
+    report(f"recon gram {M}x{N}x{K}", rel_vs_direct_exact=rel, G_normwise=float(nrm))
+    assert rel <= 2e-3
+    assert nrm <= 2.0 ** -8
+
+
+def test_gram_entry_points_reject_bad_shapes(dev):
+    import torch
+    import post_weight_quantization_philox_amd as g
+    XT = torch.zeros((64 * 128,), dtype=torch.bfloat16, device=dev)
+    H = torch.zeros((128, 128), dtype=torch.bfloat16, device=dev)
+    for tokens, cols in [(63, 128), (64, 100), (0, 128)]:
+        with pytest.raises(g.GsqError):
+            g.gsq_gram(tokens, cols, XT, H)
+    assert g.gsq_recon_gram_workspace_bytes(10, 100) == 0
+    ws = torch.zeros((64,), dtype=torch.float32, device=dev)
+    G = torch.zeros((4, 128), dtype=torch.float32, device=dev)
+    loss = torch.zeros((1,), dtype=torch.float64, device=dev)
+    with pytest.raises(g.GsqError):       # workspace too small
+        g.gsq_recon_gram(4, 128, H, H, ws, G, loss, workspace_bytes=4)
+
+
 # ----------------------------------------------------------------------------
 # Hardening and packing
 # ----------------------------------------------------------------------------
