@@ -10,6 +10,9 @@ bf16 N(0,1) activations with 1 % outlier channels x20, Lion lr 1e-3.
 Prints one JSON line: weights/s over the timed steps, per-call times from HIP
 events recorded on the launch stream, the roofline of the dominant kernel,
 and the CPU oracle's rate on a bounded sample of the same workload.
+``--workload`` times one of the other synthetic layers instead (ternary
+down_proj, 3-bit local-shift gate_proj, the 64-expert batch, the 512x512
+layer); the default is the q_proj layer above.
 """
 
 from __future__ import annotations
@@ -27,15 +30,25 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 WORKLOAD = "qproj4096_int2"
-# Algorithmic bytes per weight coordinate per call (2-bit grid, L = 4 fp32
-# logits, bf16 W): forward reads 4 logits + W and writes dW (16 + 2 + 2);
-# backward reads G, 4 logits, 4 momenta and writes 4 logits, 4 momenta
-# (4 + 16 + 16 + 16 + 16); the fused backward + next forward adds W and dW
-# (68 + 2 + 2). Group scale traffic (< 0.2 B) is left out.
-FWD_BYTES_PER_COORD = 20
-BWD_BYTES_PER_COORD = 68
-FUSED_BYTES_PER_COORD = 72
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qproj4096_int2.json")
+N_LOGITS = {0: 4, 1: 2, 2: 5}    # 2-bit, ternary, 3-bit local shift
+
+
+def bytes_per_coord(grid: int, w_bf16: bool) -> dict:
+    """Algorithmic bytes per weight coordinate per call. Forward: L fp32
+    logits + W read, dW (bf16) written. Backward + Lion: G, L logits and L
+    momenta read, L logits and L momenta written. The fused backward + next
+    forward adds W and dW. Local shift also reads its 1-byte warm-start code
+    (once in the fused pass). Group scale traffic (< 0.2 B) is left out.
+    2-bit bf16: 20 / 68 / 72 B."""
+    L = N_LOGITS[grid]
+    wb = 2 if w_bf16 else 4
+    code = 1 if grid == 2 else 0
+    return {"fwd": 4 * L + wb + 2 + code, "bwd": 4 + 16 * L + code,
+            "fused": 4 + 16 * L + wb + 2 + code}
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
 def kernel_source_hash() -> str:
@@ -47,11 +60,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, launches_bytes: float):
+def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed counter runs, if they were
     taken on the current kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -62,8 +75,8 @@ def measured_traffic(kernel: str, launches_bytes: float):
 
 
 def cpu_baseline(data, rows: int):
-    """The oracle (NumPy fp64) on the first ``rows`` rows of the layer: one
-    full step (relaxed forward, both products against all 4096 tokens,
+    """The oracle (NumPy fp64) on the first ``rows`` rows of a dense layer:
+    one full step (relaxed forward, both products against all tokens,
     backward, Lion on logits and scales)."""
     import numpy as np
     import oracle
@@ -72,19 +85,33 @@ def cpu_baseline(data, rows: int):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:            # threadpoolctl missing: report one thread
         blas_threads = 1
+    wl = data["workload"]
     W = data["W"][:rows]
     X = data["X"]
-    scales, codes, logits = oracle.init_rtn(W, oracle.GRID_INT2)
+    scales, codes, logits = oracle.init_rtn(W, wl.grid)
     state = {"logits": logits, "mom": np.zeros_like(logits), "scales": scales,
              "scale_mom": np.zeros_like(scales), "codes": codes}
     t0 = time.perf_counter()
-    oracle.step(state, W, X, oracle.GRID_INT2, 0, 1.0, 0, 0, 1e-3, 1e-5, bf16_dW=True)
+    oracle.step(state, W, X, wl.grid, 0, 1.0, 0, 0, 1e-3, 1e-5, bf16_dW=True)
     dt = time.perf_counter() - t0
     return {"value": rows * W.shape[1] / dt, "unit": "weights/s", "cores": blas_threads,
             "kind": "oracle",
-            "sample": f"one full step on rows 0..{rows - 1} of the 4096x4096 layer "
-                      f"({rows * W.shape[1]} weights) against all 4096 tokens, {dt:.1f} s; "
+            "sample": f"one full step on rows 0..{rows - 1} of the {wl.rows}x{wl.cols} layer "
+                      f"({rows * W.shape[1]} weights) against all {X.shape[0]} tokens, {dt:.1f} s; "
                       f"NumPy elementwise work on one thread, BLAS on {blas_threads}"}
+
+
+def describe(wl) -> str:
+    grid = {0: "2-bit grid (4 fp32 logits/weight)", 1: "ternary mask+sign (2 fp32 logits/weight)",
+            2: "3-bit local shift (5 fp32 logits/weight)"}[wl.grid]
+    x = {"normal": "N(0,1)", "normal_outliers": "N(0,1) with 1% outlier channels x20",
+         "student_t4": "Student-t(4)"}[wl.x_kind]
+    w = "bf16" if wl.w_bf16 else "fp32"
+    if wl.experts > 1:
+        return (f"{wl.experts} experts of {wl.rows_per_expert}x{wl.cols} {w}, {grid}, group 128, "
+                f"routed tokens per expert ~ Zipf({wl.extra['zipf_a']}) on "
+                f"[{wl.extra['n_min']}, {wl.extra['n_max']}], bf16 {x}")
+    return f"{wl.rows}x{wl.cols} {w}, {grid}, group 128, {wl.tokens} tokens bf16 {x}"
 
 
 def time_fused(solver, taus, warmup: int, steps: int, stream):
@@ -120,7 +147,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the oracle sample (default: about 1.4e11 flops of products)")
+    ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--unfused", action="store_true",
                     help="time separate forward and backward calls instead of the fused pass")
     ap.add_argument("--no-variants", action="store_true",
@@ -142,14 +171,20 @@ def main():
         sys.exit(1)
     g.lib()
     dev = torch.device("cuda:0")
-    data = synthetic.generate(WORKLOAD, seed=0)
+    data = synthetic.generate(args.workload, seed=0)
     wl = data["workload"]
-    Wd = torch.from_numpy(data["W_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    if wl.w_bf16:
+        Wd = torch.from_numpy(data["W_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        Wd = torch.from_numpy(data["W"]).to(dev)
     Xd = torch.from_numpy(data["X_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
-    solver = LayerSolver(Wd, Xd, g.GRID_INT2, seed=0, stream_id=0,
-                         lion=g.GsqLion.make(lr_logit=wl.lr_logit, lr_scale=1e-5))
+    lion = g.GsqLion.make(lr_logit=wl.lr_logit, lr_scale=1e-5)
+    solver = LayerSolver(Wd, Xd, wl.grid, tok_offsets=data["tok_offsets"],
+                         rows_per_expert=wl.rows_per_expert or None, seed=0, stream_id=0, lion=lion)
     M, K, N = solver.rows, solver.cols, solver.tokens
     coords = M * K
+    bpc = bytes_per_coord(wl.grid, wl.w_bf16)
+    FWD_BYTES_PER_COORD, BWD_BYTES_PER_COORD, FUSED_BYTES_PER_COORD = bpc["fwd"], bpc["bwd"], bpc["fused"]
 
     # A plain copy of known size, untimed: its counter readings calibrate
     # FETCH_SIZE / WRITE_SIZE in the profiler runs.
@@ -159,7 +194,11 @@ def main():
 
     taus = tau_schedule(args.warmup + args.steps + 1)
     stream = torch.cuda.current_stream()
-    gemm_flops = 4.0 * N * M * K
+    # two products of 2*n_e*rows_e*K flops per expert (N = padded token total)
+    rpe = solver.rows_per_expert
+    gemm_flops = 4.0 * rpe * K * float(N)
+    offs = [int(o) for o in solver.tok_offsets]
+    n_gemm = 2 * max(1, sum(1 for e in range(len(offs) - 1) if offs[e + 1] > offs[e]))
     if args.unfused:
         for t in range(args.warmup):
             solver.step(t, taus[t])
@@ -187,7 +226,8 @@ def main():
                                 "note": "two bf16 GEMMs (2NMK flops each) + loss finalize"},
             "relax_bwd_lion": {"ms": bwd_ms, "GB/s": BWD_BYTES_PER_COORD * coords / bwd_ms / 1e6},
         }
-        per_launch = {"relax_fwd": fwd_ms, "recon_loss_grad": rec_ms / 2, "relax_bwd_lion": bwd_ms}
+        per_launch = {"relax_fwd": fwd_ms, "recon_loss_grad": rec_ms / n_gemm,
+                      "relax_bwd_lion": bwd_ms}
         bytes_per = {"relax_fwd": FWD_BYTES_PER_COORD, "relax_bwd_lion": BWD_BYTES_PER_COORD}
     else:
         elapsed, rec_ms, fus_ms = time_fused(solver, taus, args.warmup, args.steps, stream)
@@ -198,14 +238,14 @@ def main():
                                    "GB/s": FUSED_BYTES_PER_COORD * coords / fus_ms / 1e6,
                                    "note": "backward + Lion of step t and forward of step t+1"},
         }
-        per_launch = {"recon_loss_grad": rec_ms / 2, "relax_bwd_lion_fwd": fus_ms}
+        per_launch = {"recon_loss_grad": rec_ms / n_gemm, "relax_bwd_lion_fwd": fus_ms}
         bytes_per = {"relax_bwd_lion_fwd": FUSED_BYTES_PER_COORD}
     loss = float(solver.loss.item())
     ms_per_step = elapsed * 1e3 / args.steps
 
-    # Dominant single kernel: the recon call is two GEMM launches (equal
-    # flops) plus a few-microsecond loss finalize, so each GEMM launch is
-    # weighed at half the call.
+    # Dominant single kernel: the recon call is two GEMM launches per expert
+    # (equal flops) plus a few-microsecond loss finalize, so each GEMM launch
+    # is weighed at its share of the call.
     dominant = max(per_launch, key=per_launch.get)
     if dominant == "recon_loss_grad":
         ach = kernels[dominant]["TFLOP/s"]
@@ -217,7 +257,7 @@ def main():
         ach = kernels[dominant]["GB/s"]
         roof = {"bound": "hbm", "kernel": dominant + "_kernel", "achieved": ach,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                "traffic": measured_traffic(dominant, per * coords),
+                "traffic": measured_traffic(args.workload, dominant),
                 "algorithmic_bytes_per_launch": per * coords}
 
     out = {
@@ -233,22 +273,22 @@ def main():
         "vs_baseline": None,
         "dtype": "f32 relax+Lion, bf16 MFMA (fp32 accumulate)",
         "data": "synthetic",
-        "config": {"workload": "q_proj 4096x4096 bf16, 2-bit grid (4 fp32 logits/weight), "
-                               "group 128, 4096 tokens bf16 N(0,1) with 1% outlier channels x20",
-                   "rows": M, "cols": K, "tokens": N, "grid": "int2", "lion_lr": wl.lr_logit},
+        "config": {"workload": describe(wl), "name": wl.name,
+                   "rows": M, "cols": K, "tokens": int(data["tok_offsets"][-1]),
+                   "experts": wl.experts, "grid": ["int2", "ternary", "int3_local"][wl.grid],
+                   "lion_lr": wl.lr_logit},
         "roofline": roof,
         "kernels": kernels,
         "last_loss": loss,
     }
-    if not args.no_variants and not args.unfused:
+    if not args.no_variants and not args.unfused and wl.experts == 1:
         # Same step with the objective in Gram form (H = X^T X formed once,
         # untimed; one product of 2*M*K*K flops per step instead of two of
         # 2*N*M*K), on a fresh solver. Reported beside the headline, which
         # keeps the two-product form.
         del solver
         torch.cuda.empty_cache()
-        gsol = LayerSolver(Wd, Xd, g.GRID_INT2, seed=0, stream_id=0, recon="gram",
-                           lion=g.GsqLion.make(lr_logit=wl.lr_logit, lr_scale=1e-5))
+        gsol = LayerSolver(Wd, Xd, wl.grid, seed=0, stream_id=0, recon="gram", lion=lion)
         g_el, g_rec, g_fus = time_fused(gsol, taus, args.warmup, args.steps, stream)
         gram_flops = 2.0 * M * K * K
         out["variants"] = {"gram": {
@@ -261,8 +301,9 @@ def main():
             "last_loss": float(gsol.loss.item()),
         }}
         del gsol
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(data, args.cpu_rows)
+    if not args.no_cpu_baseline and wl.experts == 1:
+        rows = args.cpu_rows or max(64, min(M, int(4096 * 4096 * 4096 // (K * N)) // 64 * 64))
+        out["cpu_baseline"] = cpu_baseline(data, rows)
     print(json.dumps(out), flush=True)
 
 

@@ -56,18 +56,68 @@ struct GemmArgs {
     int64_t ldd;
 };
 
-__device__ __forceinline__ void tile_of(const GemmArgs& g, int& ti, int& tj) {
+// Experts of one grouped launch (at most kMaxGroups). Expert e of the launch
+// (expert0 + e of the batch) owns rows [e*rpe, (e+1)*rpe) of dW, R^T's block
+// and G, and the token block [tok[e], tok[e+1]) of X (absolute offsets,
+// multiples of 64); its workgroups are [wg0[e], wg0[e+1]).
+constexpr int kMaxGroups = 64;
+struct ExpertBatch {
+    int n;            // experts in this launch
+    int stage;        // 0: R_e^T = dW_e X_e^T;  1: G_e = 2 R_e^T X_e
+    int rpe, cols, expert0;
+    const uint16_t* dW;
+    const uint16_t* X;
+    const uint16_t* XT;
+    uint16_t* RT;
+    float* G;
+    int tok[kMaxGroups + 1];
+    int wg0[kMaxGroups + 1];
+};
+
+// Workgroups are renumbered so that consecutive logical indices share an XCD
+// (the dispatcher deals workgroups round-robin over the 8 XCDs).
+__device__ __forceinline__ int logical_wg() {
     const int nwg = gridDim.x;
     const int wg = blockIdx.x;
-    int logical = wg;
-    if ((nwg & 7) == 0) logical = (wg & 7) * (nwg >> 3) + (wg >> 3);
-    const int width = kGroupM * g.tiles_j;
+    return (nwg & 7) == 0 ? (wg & 7) * (nwg >> 3) + (wg >> 3) : wg;
+}
+
+// Tile of a logical index inside a tiles_i x tiles_j grid, in groups of
+// kGroupM tile-rows.
+__device__ __forceinline__ void tile_of(int logical, int tiles_i, int tiles_j, int& ti, int& tj) {
+    const int width = kGroupM * tiles_j;
     const int grp = logical / width;
     const int first = grp * kGroupM;
-    const int gm = min(g.tiles_i - first, kGroupM);
+    const int gm = min(tiles_i - first, kGroupM);
     const int in = logical - grp * width;
     ti = first + in % gm;
     tj = in / gm;
+}
+
+// The product this workgroup's expert computes, and the workgroup's index
+// within it.
+__device__ __forceinline__ int resolve(const ExpertBatch& eb, int logical, GemmArgs& g) {
+    int e = 0;
+    for (int k = 1; k < eb.n; ++k) e = logical >= eb.wg0[k] ? k : e;
+    const int64_t t0 = eb.tok[e];
+    const int ne = eb.tok[e + 1] - eb.tok[e];
+    const int64_t rows0 = static_cast<int64_t>(eb.expert0 + e) * eb.rpe;
+    if (eb.stage == 0) {
+        g.A = eb.dW + rows0 * eb.cols; g.lda = eb.cols;
+        g.B = eb.X + t0 * eb.cols;     g.ldb = eb.cols;
+        g.I = eb.rpe; g.J = ne; g.Rd = eb.cols;
+        g.C = eb.RT + static_cast<int64_t>(eb.rpe) * t0; g.ldc = ne;
+        g.a_bytes = eb.rpe * eb.cols * 2; g.b_bytes = ne * eb.cols * 2;
+    } else {
+        g.A = eb.RT + static_cast<int64_t>(eb.rpe) * t0; g.lda = ne;
+        g.B = eb.XT + static_cast<int64_t>(eb.cols) * t0; g.ldb = ne;
+        g.I = eb.rpe; g.J = eb.cols; g.Rd = ne;
+        g.C = eb.G + rows0 * eb.cols; g.ldc = eb.cols;
+        g.a_bytes = eb.rpe * ne * 2; g.b_bytes = eb.cols * ne * 2;
+    }
+    g.tiles_i = (g.I + BM - 1) / BM;
+    g.tiles_j = (g.J + BN - 1) / BN;
+    return logical - eb.wg0[e];
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -105,15 +155,19 @@ __device__ __forceinline__ void bar() {
     asm volatile("" ::: "memory");
 }
 
-template <int EPI>
-__global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
+// GROUPED: one launch over the experts of `eb` (its product replaces the
+// operand fields of g); otherwise g is one product and eb is unused.
+template <int EPI, bool GROUPED>
+__global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb) {
     __shared__ uint4 sA0[BM * kChunks];
     __shared__ uint4 sB0[BN * kChunks];
     __shared__ uint4 sA1[BM * kChunks];
     __shared__ uint4 sB1[BN * kChunks];
 
+    int local = logical_wg();
+    if constexpr (GROUPED) local = resolve(eb, local, g);
     int ti, tj;
-    tile_of(g, ti, tj);
+    tile_of(local, g.tiles_i, g.tiles_j, ti, tj);
     const int i0 = ti * BM, j0 = tj * BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -229,39 +283,42 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g) {
 
     const int nk = g.Rd / BK;
     constexpr uint32_t kStep = BK * 2;   // bytes of one K-step along a row
-    // Prologue: step 0 (waited for) and step 1 in flight; slices 0-1 fetched.
-    dma_tile(ra_rs, oa, 0, sA0, wave);
-    dma_tile(rb_rs, ob, 0, sB0, wave);
-    if (nk > 1) {
-        wait_dma();
-        dma_tile(ra_rs, oa, kStep, sA1, wave);
-        dma_tile(rb_rs, ob, kStep, sB1, wave);
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    } else {
-        wait_dma();
-    }
-    bar();
+    // An expert without tokens has an empty contraction: its output is zero.
+    if (nk > 0) {
+        // Prologue: step 0 (waited for) and step 1 in flight; slices 0-1 fetched.
+        dma_tile(ra_rs, oa, 0, sA0, wave);
+        dma_tile(rb_rs, ob, 0, sB0, wave);
+        if (nk > 1) {
+            wait_dma();
+            dma_tile(ra_rs, oa, kStep, sA1, wave);
+            dma_tile(rb_rs, ob, kStep, sB1, wave);
+            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        } else {
+            wait_dma();
+        }
+        bar();
 #pragma unroll
-    for (int part = 0; part < 4; ++part) {
-        fetch2(sA0, sB0, 0, part);
-        fetch2(sA0, sB0, 1, part);
-    }
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt) {
-        const bool odd = kt & 1;
-        kstep(std::true_type{}, std::true_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0,
-              odd ? sA0 : sA1, odd ? sB0 : sB1, static_cast<uint32_t>(kt + 2) * kStep);
-    }
-    if (kt + 1 < nk) {
-        const bool odd = kt & 1;
-        kstep(std::true_type{}, std::false_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0,
-              odd ? sA0 : sA1, odd ? sB0 : sB1, 0u);
-        ++kt;
-    }
-    {
-        const bool odd = kt & 1;
-        kstep(std::false_type{}, std::false_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0, nullptr,
-              nullptr, 0u);
+        for (int part = 0; part < 4; ++part) {
+            fetch2(sA0, sB0, 0, part);
+            fetch2(sA0, sB0, 1, part);
+        }
+        int kt = 0;
+        for (; kt + 2 < nk; ++kt) {
+            const bool odd = kt & 1;
+            kstep(std::true_type{}, std::true_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0,
+                  odd ? sA0 : sA1, odd ? sB0 : sB1, static_cast<uint32_t>(kt + 2) * kStep);
+        }
+        if (kt + 1 < nk) {
+            const bool odd = kt & 1;
+            kstep(std::true_type{}, std::false_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0,
+                  odd ? sA0 : sA1, odd ? sB0 : sB1, 0u);
+            ++kt;
+        }
+        {
+            const bool odd = kt & 1;
+            kstep(std::false_type{}, std::false_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0, nullptr,
+                  nullptr, 0u);
+        }
     }
     // All waves are done with the operand buffers before the epilogue reuses them.
     __syncthreads();
@@ -404,7 +461,59 @@ hipError_t run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t l
     g.tiles_i = cdiv(I, BM); g.tiles_j = cdiv(J, BN);
     g.C = C; g.alpha = alpha; g.partials = partials;
     const int nwg = g.tiles_i * g.tiles_j;
-    hipLaunchKernelGGL(gemm_nt_kernel<EPI>, dim3(nwg), dim3(NT), 0, st, g);
+    ExpertBatch none{};
+    hipLaunchKernelGGL((gemm_nt_kernel<EPI, false>), dim3(nwg), dim3(NT), 0, st, g, none);
+    return hipGetLastError();
+}
+
+// Both products of every expert in [e0, e1) (at most kMaxGroups), one grouped
+// launch per product; stage-0 partials start at `partials`. Returns the
+// number of partials written.
+hipError_t run_expert_batch(int e0, int e1, const int64_t* tok_offsets, int64_t rpe, int64_t cols,
+                            const uint16_t* X, const uint16_t* XT, const uint16_t* dW,
+                            float* partials, uint16_t* RT, float* G, hipStream_t st,
+                            size_t* n_partials) {
+    ExpertBatch eb{};
+    eb.n = e1 - e0;
+    eb.rpe = static_cast<int>(rpe);
+    eb.cols = static_cast<int>(cols);
+    eb.expert0 = e0;
+    eb.dW = dW; eb.X = X; eb.XT = XT; eb.RT = RT; eb.G = G;
+    // Per-expert operands are addressed like run_gemm's: 32-bit byte offsets
+    // that must stay below kOob minus the contraction length.
+    const int64_t lim = static_cast<int64_t>(kOob) - 2 * cols - 2 * tok_offsets[e1];
+    if (rpe * cols * 2 > lim) return hipErrorInvalidValue;
+    for (int e = e0; e < e1; ++e) {
+        const int64_t ne = tok_offsets[e + 1] - tok_offsets[e];
+        if (ne * cols * 2 > lim || rpe * ne * 2 > lim) return hipErrorInvalidValue;
+    }
+    const int ti = cdiv(rpe, BM);
+    int wg1 = 0, wg2 = 0;
+    int wg0_2[kMaxGroups + 1];
+    for (int e = 0; e <= eb.n; ++e) eb.tok[e] = static_cast<int>(tok_offsets[e0 + e]);
+    for (int e = 0; e < eb.n; ++e) {
+        eb.wg0[e] = wg1;
+        wg0_2[e] = wg2;
+        wg1 += ti * cdiv(eb.tok[e + 1] - eb.tok[e], BN);
+        wg2 += ti * cdiv(cols, BN);
+    }
+    eb.wg0[eb.n] = wg1;
+    wg0_2[eb.n] = wg2;
+    GemmArgs g{};
+    g.alpha = 1.0f;
+    g.partials = partials;
+    *n_partials = static_cast<size_t>(wg1);
+    if (wg1 > 0) {
+        eb.stage = 0;
+        hipLaunchKernelGGL((gemm_nt_kernel<EPI_BF16_LOSS, true>), dim3(wg1), dim3(NT), 0, st, g, eb);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    eb.stage = 1;
+    for (int e = 0; e <= eb.n; ++e) eb.wg0[e] = wg0_2[e];
+    g.alpha = 2.0f;
+    g.partials = nullptr;
+    hipLaunchKernelGGL((gemm_nt_kernel<EPI_F32_SCALED, true>), dim3(wg2), dim3(NT), 0, st, g, eb);
     return hipGetLastError();
 }
 
@@ -424,26 +533,34 @@ hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t r
                         float* partials, uint16_t* RT, float* G, double* loss, hipStream_t st) {
     size_t slot = 0;
     hipError_t err = hipSuccess;
-    for (int e = 0; e < n_experts && err == hipSuccess; ++e) {
-        const int64_t t0 = tok_offsets[e];
-        const int64_t ne = tok_offsets[e + 1] - t0;
-        const uint16_t* dWe = dW + static_cast<int64_t>(e) * rows_per_expert * cols;
-        float* Ge = G + static_cast<int64_t>(e) * rows_per_expert * cols;
+    if (n_experts == 1) {
+        // One dense layer: two plain launches.
+        const int64_t ne = tok_offsets[1];
         if (ne == 0) {
             const int64_t n = rows_per_expert * cols;
-            hipLaunchKernelGGL(fill_zero_kernel, dim3(cdiv(n, 256)), dim3(256), 0, st, Ge, n);
+            hipLaunchKernelGGL(fill_zero_kernel, dim3(cdiv(n, 256)), dim3(256), 0, st, G, n);
             err = hipGetLastError();
-            continue;
+        } else {
+            err = run_gemm<EPI_BF16_LOSS>(dW, cols, X, cols, static_cast<int>(rows_per_expert),
+                                          static_cast<int>(ne), static_cast<int>(cols), RT, ne,
+                                          1.0f, partials, st);
+            if (err == hipSuccess) {
+                slot = static_cast<size_t>(cdiv(rows_per_expert, BM)) * cdiv(ne, BN);
+                err = run_gemm<EPI_F32_SCALED>(RT, ne, XT, ne, static_cast<int>(rows_per_expert),
+                                               static_cast<int>(cols), static_cast<int>(ne), G,
+                                               cols, 2.0f, nullptr, st);
+            }
         }
-        uint16_t* RTe = RT + rows_per_expert * t0;
-        err = run_gemm<EPI_BF16_LOSS>(dWe, cols, X + t0 * cols, cols, static_cast<int>(rows_per_expert),
-                                      static_cast<int>(ne), static_cast<int>(cols), RTe, ne, 1.0f,
-                                      partials + slot, st);
-        if (err != hipSuccess) break;
-        slot += static_cast<size_t>(cdiv(rows_per_expert, BM)) * cdiv(ne, BN);
-        err = run_gemm<EPI_F32_SCALED>(RTe, ne, XT + cols * t0, ne, static_cast<int>(rows_per_expert),
-                                       static_cast<int>(cols), static_cast<int>(ne), Ge, cols, 2.0f,
-                                       nullptr, st);
+    } else {
+        // Expert batches: every expert's tiles in one launch per product
+        // (an expert's own products are too small to fill the GPU).
+        for (int e0 = 0; e0 < n_experts && err == hipSuccess; e0 += kMaxGroups) {
+            const int e1 = e0 + kMaxGroups < n_experts ? e0 + kMaxGroups : n_experts;
+            size_t np = 0;
+            err = run_expert_batch(e0, e1, tok_offsets, rows_per_expert, cols, X, XT, dW,
+                                   partials + slot, RT, G, st, &np);
+            slot += np;
+        }
     }
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(256), 0, st, partials,
