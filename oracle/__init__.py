@@ -14,7 +14,7 @@ forms, finite differences, brute force, the numbers the pages print).
 
 from .philox import (philox4x32_10, noise_words, uniform_from_word, gumbel,
                      logistic)
-from .gsq import (GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL, N_LOGITS, Q_MAX,
+from .gsq import (GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL, GRID_INT3, N_LOGITS, Q_MAX,
                   CODE_BITS, LOCAL_OFFSETS, level_value, grid_levels,
                   candidate_codes, init_rtn, noise, relax_probs, ternary_terms,
                   relax_fwd, relax_bwd, recon_loss_grad,

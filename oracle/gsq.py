@@ -46,13 +46,17 @@ from .philox import noise_words, uniform_from_word, gumbel, logistic
 GRID_INT2 = 0
 GRID_TERNARY = 1
 GRID_INT3_LOCAL = 2
+#: 3 bits with one logit per level of the whole 8-level grid: the baseline that
+#: local shift approximates (agihunt.info, method paragraph: eight logits for
+#: 3 bits without the shift).
+GRID_INT3 = 3
 
-#: logits per coordinate (agihunt.info, method paragraph: 4, 2 and 5).
-N_LOGITS = {GRID_INT2: 4, GRID_TERNARY: 2, GRID_INT3_LOCAL: 5}
+#: logits per coordinate (agihunt.info, method paragraph: 4, 2, 5 and 8).
+N_LOGITS = {GRID_INT2: 4, GRID_TERNARY: 2, GRID_INT3_LOCAL: 5, GRID_INT3: 8}
 #: largest grid magnitude in units of the scale.
-Q_MAX = {GRID_INT2: 3, GRID_TERNARY: 1, GRID_INT3_LOCAL: 7}
+Q_MAX = {GRID_INT2: 3, GRID_TERNARY: 1, GRID_INT3_LOCAL: 7, GRID_INT3: 7}
 #: bits per stored code (ternary codes t+1 in {0,1,2} take 2 bits).
-CODE_BITS = {GRID_INT2: 2, GRID_TERNARY: 2, GRID_INT3_LOCAL: 3}
+CODE_BITS = {GRID_INT2: 2, GRID_TERNARY: 2, GRID_INT3_LOCAL: 3, GRID_INT3: 3}
 #: offsets of the local-shift candidates around the warm-start code.
 LOCAL_OFFSETS = (-2, -1, 0, 1, 2)
 
@@ -74,7 +78,7 @@ def grid_levels(grid: int) -> np.ndarray:
     """All grid values of a grid, in scale units."""
     if grid == GRID_INT2:
         return level_value(np.arange(4), 2).astype(np.float64)
-    if grid == GRID_INT3_LOCAL:
+    if grid in (GRID_INT3_LOCAL, GRID_INT3):
         return level_value(np.arange(8), 3).astype(np.float64)
     if grid == GRID_TERNARY:
         return np.array([-1.0, 0.0, 1.0])
@@ -84,14 +88,16 @@ def grid_levels(grid: int) -> np.ndarray:
 def candidate_codes(grid: int, init_codes: np.ndarray) -> np.ndarray:
     """Codes the L logits of each coordinate stand for, shape [L, ...].
 
-    2-bit: the four codes 0..3 for every coordinate. Local shift: the warm-start
-    code plus offsets -2..+2, clamped to the 8-level range [0, 7] (so edge
-    coordinates carry duplicate candidates).
+    2-bit: the four codes 0..3 for every coordinate; full 3-bit: the eight
+    codes 0..7. Local shift: the warm-start code plus offsets -2..+2, clamped
+    to the 8-level range [0, 7] (so edge coordinates carry duplicate
+    candidates).
     """
-    if grid == GRID_INT2:
+    if grid in (GRID_INT2, GRID_INT3):
+        L = N_LOGITS[grid]
         shape = init_codes.shape if init_codes is not None else ()
-        return np.broadcast_to(np.arange(4).reshape((4,) + (1,) * len(shape)),
-                               (4,) + tuple(shape)).astype(np.int64)
+        return np.broadcast_to(np.arange(L).reshape((L,) + (1,) * len(shape)),
+                               (L,) + tuple(shape)).astype(np.int64)
     if grid == GRID_INT3_LOCAL:
         c0 = np.asarray(init_codes, dtype=np.int64)
         return np.stack([np.clip(c0 + d, 0, 7) for d in LOCAL_OFFSETS])
@@ -113,7 +119,8 @@ def init_rtn(W, grid: int, group: int = 128, init_logit: float = 2.0):
     Decisions in fp32: s = maxabs/q_max and x = w/s are correctly rounded fp32
     divisions; u = (x + q_max)*0.5 in fp32; the code is rint(u) (ties to even),
     clamped to the grid. A zero scale gives x = 0.
-    Logits: +init_logit on the warm-start level, 0 on the others; ternary sets
+    Logits: +init_logit on the warm-start level, 0 on the others (local shift:
+    the warm-start level is offset 0, logit index 2); ternary sets
     the mask logit to +init_logit if t0 != 0 else -init_logit, and the sign
     logit to +init_logit if w >= 0 else -init_logit.
     """
@@ -141,8 +148,8 @@ def init_rtn(W, grid: int, group: int = 128, init_logit: float = 2.0):
         u = ((x + qmax).astype(np.float32) * np.float32(0.5)).astype(np.float32)
         c0 = np.clip(np.rint(u), 0, 2 ** bits - 1).astype(np.int64)
         codes = c0.astype(np.uint8)
-        if grid == GRID_INT2:
-            for k in range(4):
+        if grid in (GRID_INT2, GRID_INT3):
+            for k in range(L):
                 logits[k] = np.where(c0 == k, il, np.float32(0))
         else:
             logits[2] = il
@@ -199,7 +206,7 @@ def relax_probs(logits, grid: int, seed: int, stream: int, step: int,
                 tau: float, noise_scale: float, row0: int = 0):
     """Gumbel-Softmax probabilities at temperature tau.
 
-    2-bit / local shift: p = softmax((l + eta*g)/tau) over the L logits.
+    2-bit / 3-bit / local shift: p = softmax((l + eta*g)/tau) over the L logits.
     Ternary: a = sigmoid((l_m + eta*n_m)/tau) (mask on),
     b = sigmoid((l_s + eta*n_s)/tau) (sign positive).
     """
@@ -215,8 +222,9 @@ def relax_probs(logits, grid: int, seed: int, stream: int, step: int,
 
 
 def _values(grid: int, init_codes, shape):
-    if grid == GRID_INT2:
-        return level_value(np.arange(4), 2).astype(np.float64).reshape(4, 1, 1) \
+    if grid in (GRID_INT2, GRID_INT3):
+        L, bits = N_LOGITS[grid], CODE_BITS[grid]
+        return level_value(np.arange(L), bits).astype(np.float64).reshape(L, 1, 1) \
             * np.ones((1,) + tuple(shape))
     return level_value(candidate_codes(grid, init_codes), 3).astype(np.float64)
 
@@ -399,16 +407,16 @@ def lion(theta, grad, mom, lr: float, beta1: float, beta2: float,
 def harden(logits, grid: int, init_codes=None) -> np.ndarray:
     """Noise-free hard codes after annealing (stored form, uint8).
 
-    2-bit: argmax of the four logits (first index on ties). Local shift:
-    clamp(c0 + argmax - 2, 0, 7). Ternary: t = [l_m >= 0] * (+1 if l_s >= 0
-    else -1), stored as t + 1.
+    2-bit / full 3-bit: argmax of the logits (first index on ties). Local
+    shift: clamp(c0 + argmax - 2, 0, 7). Ternary: t = [l_m >= 0] * (+1 if
+    l_s >= 0 else -1), stored as t + 1.
     """
     lg = np.asarray(logits, dtype=np.float32)
     if grid == GRID_TERNARY:
         t = np.where(lg[0] >= 0, np.where(lg[1] >= 0, 1, -1), 0)
         return (t + 1).astype(np.uint8)
     k = np.argmax(lg, axis=0)
-    if grid == GRID_INT2:
+    if grid in (GRID_INT2, GRID_INT3):
         return k.astype(np.uint8)
     c0 = np.asarray(init_codes, dtype=np.int64)
     return np.clip(c0 + k - 2, 0, 7).astype(np.uint8)

@@ -15,10 +15,10 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL
+from oracle import GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL, GRID_INT3
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-GRIDS = [GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL]
+GRIDS = [GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL, GRID_INT3]
 
 
 def layer(M, K, seed=0, sigma=0.02):
@@ -33,7 +33,7 @@ def rand_logits(grid, M, K, seed=1, spread=1.5):
 # Softmax, limits and closed forms
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("grid", [GRID_INT2, GRID_INT3_LOCAL])
+@pytest.mark.parametrize("grid", [GRID_INT2, GRID_INT3_LOCAL, GRID_INT3])
 @pytest.mark.parametrize("tau", [1.0, 0.3, 0.05])
 def test_softmax_rows_sum_to_one(grid, tau):
     p = oracle.relax_probs(rand_logits(grid, 4, 256), grid, 0, 0, 3, tau, 1.0)
@@ -58,7 +58,7 @@ def test_tau_to_zero_gives_argmax_grid_point(grid):
         ys = np.sort(y, axis=0)
         ok = (ys[-1] - ys[-2]) > 1e-2
         k = np.argmax(y, axis=0)
-        codes = k if grid == GRID_INT2 else np.clip(c0.astype(np.int64) + k - 2, 0, 7)
+        codes = k if grid in (GRID_INT2, GRID_INT3) else np.clip(c0.astype(np.int64) + k - 2, 0, 7)
         hard = oracle.level_value(codes, oracle.CODE_BITS[grid])
     assert ok.mean() > 0.95
     np.testing.assert_allclose(w[ok], (sfull * hard)[ok], rtol=1e-12, atol=0)
@@ -71,6 +71,28 @@ def test_zero_noise_uniform_logits_2bit_is_grid_mean():
     f = oracle.relax_fwd(np.zeros((4, M, K)), s, W, GRID_INT2, 0, 0, 0, 0.37, 0.0)
     # mean of {-3, -1, 1, 3} is 0
     assert np.max(np.abs(f["w_soft"])) < 1e-15
+    # and of the eight levels -7..7 of the full 3-bit grid
+    s3, _, _ = oracle.init_rtn(W, GRID_INT3)
+    f3 = oracle.relax_fwd(np.zeros((8, M, K)), s3, W, GRID_INT3, 0, 0, 0, 0.37, 0.0)
+    assert np.max(np.abs(f3["w_soft"])) < 1e-15
+
+
+def test_full_grid_restricted_to_window_is_local_shift():
+    # Noise-free, the full 3-bit relaxation with every level outside c0 +- 2
+    # switched off (logit -1e4) is the local-shift relaxation of the same
+    # five logits, for warm-start codes away from the edges.
+    rng = np.random.default_rng(12)
+    K = 128
+    c0 = rng.integers(2, 6, size=(1, K)).astype(np.uint8)
+    loc = rng.normal(0, 1.5, (5, 1, K))
+    full = np.full((8, 1, K), -1e4)
+    for d in range(5):
+        np.put_along_axis(full, (c0.astype(np.int64) + d - 2)[None], loc[d][None], axis=0)
+    s = np.array([[0.013]], dtype=np.float32)
+    W = np.zeros((1, K))
+    a = oracle.relax_fwd(loc, s, W, GRID_INT3_LOCAL, 0, 0, 0, 0.6, 0.0, c0)["w_soft"]
+    b = oracle.relax_fwd(full, s, W, GRID_INT3, 0, 0, 0, 0.6, 0.0)["w_soft"]
+    np.testing.assert_allclose(b, a, rtol=1e-13, atol=1e-18)
 
 
 def test_zero_noise_uniform_logits_local_shift_closed_forms():
@@ -175,7 +197,7 @@ def test_gradients_match_finite_differences(grid, tau):
     assert np.max(np.abs(fds - gs)) <= 1e-6 * np.max(np.abs(gs))
 
 
-@pytest.mark.parametrize("grid", [GRID_INT2, GRID_INT3_LOCAL])
+@pytest.mark.parametrize("grid", [GRID_INT2, GRID_INT3_LOCAL, GRID_INT3])
 def test_logit_gradients_sum_to_zero(grid):
     # sum_k p_k (v_k - w_hat) = 0, so shifting all logits of a coordinate
     # together leaves the soft weight unchanged.
@@ -431,6 +453,10 @@ def test_harden_rules():
     ll[4, 0, :] = 1.0                     # offset +2
     np.testing.assert_array_equal(oracle.harden(ll, GRID_INT3_LOCAL, np.array([[0, 6, 3]]))[0],
                                   [2, 7, 5])
+    lf = np.zeros((8, 1, 3))
+    lf[[6, 2], 0, 0] = 1.5                # tie between levels 2 and 6 -> 2
+    lf[7, 0, 1] = 0.1
+    np.testing.assert_array_equal(oracle.harden(lf, GRID_INT3)[0], [2, 7, 0])
 
 
 @pytest.mark.parametrize("bits,K", [(2, 128), (3, 128), (2, 384), (3, 256)])
@@ -477,8 +503,11 @@ def test_format_numbers_printed_on_the_pages():
     assert 2 ** oracle.CODE_BITS[GRID_INT3_LOCAL] == gold["logits_per_coord_full_3bit"]["value"]
     assert list(oracle.LOCAL_OFFSETS) == gold["local_shift_offsets"]["value"]
     assert oracle.N_LOGITS[GRID_TERNARY] / oracle.N_LOGITS[GRID_INT2] == gold["ternary_logit_ratio_to_2bit"]["value"]
+    assert oracle.N_LOGITS[GRID_INT3] == gold["logits_per_coord_full_3bit"]["value"]
+    # the 2-5x logit memory covers the grids GSQ uses (not the full 3-bit baseline)
     lo, hi = gold["logit_memory_ratio_range"]["value"]
-    assert min(oracle.N_LOGITS.values()) == lo and max(oracle.N_LOGITS.values()) == hi
+    used = [oracle.N_LOGITS[g] for g in (GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL)]
+    assert min(used) == lo and max(used) == hi
 
 
 def test_tau_schedule_endpoints():
