@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 WORKLOAD = "qproj4096_int2"
-N_LOGITS = {0: 4, 1: 2, 2: 5}    # 2-bit, ternary, 3-bit local shift
+N_LOGITS = {0: 4, 1: 2, 2: 5, 3: 8}    # 2-bit, ternary, 3-bit local shift, full 3-bit
 
 
 def bytes_per_coord(grid: int, w_bf16: bool) -> dict:
@@ -103,7 +103,8 @@ def cpu_baseline(data, rows: int):
 
 def describe(wl) -> str:
     grid = {0: "2-bit grid (4 fp32 logits/weight)", 1: "ternary mask+sign (2 fp32 logits/weight)",
-            2: "3-bit local shift (5 fp32 logits/weight)"}[wl.grid]
+            2: "3-bit local shift (5 fp32 logits/weight)",
+            3: "3-bit full grid (8 fp32 logits/weight)"}[wl.grid]
     x = {"normal": "N(0,1)", "normal_outliers": "N(0,1) with 1% outlier channels x20",
          "student_t4": "Student-t(4)"}[wl.x_kind]
     w = "bf16" if wl.w_bf16 else "fp32"
@@ -275,7 +276,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(wl), "name": wl.name,
                    "rows": M, "cols": K, "tokens": int(data["tok_offsets"][-1]),
-                   "experts": wl.experts, "grid": ["int2", "ternary", "int3_local"][wl.grid],
+                   "experts": wl.experts, "grid": ["int2", "ternary", "int3_local", "int3"][wl.grid],
                    "lion_lr": wl.lr_logit},
         "roofline": roof,
         "kernels": kernels,

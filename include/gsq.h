@@ -70,8 +70,15 @@ typedef enum {
  *  INT2        4 levels {-3,-1,1,3}, 4 logits per coordinate;
  *  TERNARY     {-1,0,1} as a binary mask times a binary sign, 2 logits;
  *  INT3_LOCAL  8 levels {-7,-5,...,7}; 5 logits for the codes
- *              clamp(c0 + d, 0, 7), d = -2..2, around a warm-start code c0. */
-typedef enum { GSQ_GRID_INT2 = 0, GSQ_GRID_TERNARY = 1, GSQ_GRID_INT3_LOCAL = 2 } gsq_grid;
+ *              clamp(c0 + d, 0, 7), d = -2..2, around a warm-start code c0;
+ *  INT3        the same 8 levels with one logit each (8 logits): the full
+ *              grid that local shift stands in for. */
+typedef enum {
+    GSQ_GRID_INT2 = 0,
+    GSQ_GRID_TERNARY = 1,
+    GSQ_GRID_INT3_LOCAL = 2,
+    GSQ_GRID_INT3 = 3
+} gsq_grid;
 
 typedef enum { GSQ_DTYPE_F32 = 0, GSQ_DTYPE_BF16 = 1 } gsq_dtype;
 

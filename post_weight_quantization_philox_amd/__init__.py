@@ -14,7 +14,7 @@ import ctypes
 import os
 
 __all__ = [
-    "GRID_INT2", "GRID_TERNARY", "GRID_INT3_LOCAL", "DTYPE_F32", "DTYPE_BF16",
+    "GRID_INT2", "GRID_TERNARY", "GRID_INT3_LOCAL", "GRID_INT3", "DTYPE_F32", "DTYPE_BF16",
     "GsqError", "GsqLayer", "GsqLion", "lib", "exported_symbols",
     "gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
     "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
@@ -22,10 +22,10 @@ __all__ = [
     "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd", "gsq_harden_pack", "gsq_noise_dump",
 ]
 
-GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL = 0, 1, 2
+GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL, GRID_INT3 = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
-N_LOGITS = {GRID_INT2: 4, GRID_TERNARY: 2, GRID_INT3_LOCAL: 5}
-CODE_BITS = {GRID_INT2: 2, GRID_TERNARY: 2, GRID_INT3_LOCAL: 3}
+N_LOGITS = {GRID_INT2: 4, GRID_TERNARY: 2, GRID_INT3_LOCAL: 5, GRID_INT3: 8}
+CODE_BITS = {GRID_INT2: 2, GRID_TERNARY: 2, GRID_INT3_LOCAL: 3, GRID_INT3: 3}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsq.so")
 

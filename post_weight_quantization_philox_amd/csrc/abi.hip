@@ -19,6 +19,7 @@ inline int num_logits(int grid) {
         case GSQ_GRID_INT2: return 4;
         case GSQ_GRID_TERNARY: return 2;
         case GSQ_GRID_INT3_LOCAL: return 5;
+        case GSQ_GRID_INT3: return 8;
         default: return 0;
     }
 }

@@ -4,11 +4,12 @@
 // N consecutive coordinates i0..i0+N-1 of the flattened layer (i0 = N * global
 // thread id), so every planar logit / momentum plane is read and written as
 // one N*4-byte vector per thread. 128/N threads cover one scale group of 128
-// coordinates and reduce it with lane shuffles. N is 2 for the 2-bit grid
-// (halving the registers a thread holds, so that more waves are in flight
-// to hide HBM latency) and 4 for ternary (already at full occupancy) and local
-// shift (whose 5 logits need N = 4 for the N coordinates' noise to be a whole
-// number of Philox blocks, L*N/4, so that no word is generated twice).
+// coordinates and reduce it with lane shuffles. N is 2 for the 2-bit and full
+// 3-bit grids (halving the registers a thread holds, so that more waves are
+// in flight to hide HBM latency) and 4 for ternary (already at full
+// occupancy) and local shift (whose 5 logits need N = 4 for the N
+// coordinates' noise to be a whole number of Philox blocks, L*N/4, so that no
+// word is generated twice).
 #include <type_traits>
 
 #include "gsq_internal.hpp"
@@ -25,6 +26,7 @@ template <int GRID> struct GridT;
 template <> struct GridT<GSQ_GRID_INT2> { static constexpr int L = 4; static constexpr int QMAX = 3; static constexpr int BITS = 2; static constexpr int N = 2; };
 template <> struct GridT<GSQ_GRID_TERNARY> { static constexpr int L = 2; static constexpr int QMAX = 1; static constexpr int BITS = 2; static constexpr int N = 4; };
 template <> struct GridT<GSQ_GRID_INT3_LOCAL> { static constexpr int L = 5; static constexpr int QMAX = 7; static constexpr int BITS = 3; static constexpr int N = 4; };
+template <> struct GridT<GSQ_GRID_INT3> { static constexpr int L = 8; static constexpr int QMAX = 7; static constexpr int BITS = 3; static constexpr int N = 2; };
 
 // Element i of a tensor whose planes start at wave-uniform bases. With O32
 // the byte offset of i fits 32 bits (checked by the launcher: rows*cols*4 <
@@ -196,7 +198,10 @@ __device__ __forceinline__ void relax_coord(const float (&l)[GridT<GRID>::L], co
         float sum = 0.0f, num = 0.0f;
 #pragma unroll
         for (int k = 0; k < L; ++k) {
-            r.v[k] = (GRID == GSQ_GRID_INT2) ? static_cast<float>(2 * k - 3) : local_value(c0, k);
+            // Level value 2c - (2^b - 1) of the candidate code c.
+            r.v[k] = (GRID == GSQ_GRID_INT2)   ? static_cast<float>(2 * k - 3)
+                     : (GRID == GSQ_GRID_INT3) ? static_cast<float>(2 * k - 7)
+                                               : local_value(c0, k);
             r.e[k] = hw_exp2(y[k] - ymax);
             sum += r.e[k];
             num = __builtin_fmaf(r.e[k], r.v[k], num);
@@ -379,9 +384,9 @@ __global__ __launch_bounds__(kThreads) void init_rtn_kernel(const void* __restri
             constexpr float cmax = static_cast<float>((1 << GridT<GRID>::BITS) - 1);
             const float u = __fmul_rn(__fadd_rn(x, qmax), 0.5f);
             code = static_cast<int>(fminf(fmaxf(rintf(u), 0.0f), cmax));
-            if constexpr (GRID == GSQ_GRID_INT2) {
+            if constexpr (GRID == GSQ_GRID_INT2 || GRID == GSQ_GRID_INT3) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) lg[k][c] = (k == code) ? init_logit : 0.0f;
+                for (int k = 0; k < L; ++k) lg[k][c] = (k == code) ? init_logit : 0.0f;
             } else {
 #pragma unroll
                 for (int k = 0; k < 5; ++k) lg[k][c] = (k == 2) ? init_logit : 0.0f;
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void harden_pack_kernel(
 #pragma unroll
                 for (int k = 1; k < L; ++k)
                     if (l[k][c] > bv) { bv = l[k][c]; best = k; }
-                if constexpr (GRID == GSQ_GRID_INT2) {
+                if constexpr (GRID == GSQ_GRID_INT2 || GRID == GSQ_GRID_INT3) {
                     code = static_cast<uint32_t>(best);
                 } else {
                     int cc = static_cast<int>((c0w >> (8 * c)) & 0xFF) + best - 2;
@@ -494,6 +499,7 @@ hipError_t launch_init_rtn(const LayerDesc& d, const void* W, float* scales, uin
     else GSQ_LAUNCH((init_rtn_kernel<G, false>), nb, st, W, d.mk, init_logit, scales, codes, logits);
     switch (d.grid) {
         case GSQ_GRID_INT2: GSQ_INIT(GSQ_GRID_INT2); break;
+        case GSQ_GRID_INT3: GSQ_INIT(GSQ_GRID_INT3); break;
         case GSQ_GRID_TERNARY: GSQ_INIT(GSQ_GRID_TERNARY); break;
         default: GSQ_INIT(GSQ_GRID_INT3_LOCAL); break;
     }
@@ -509,6 +515,7 @@ inline bool off32(const LayerDesc& d) { return d.mk * 4 <= 0xFFFFFFF0ull; }
 inline uint64_t relax_threads(const LayerDesc& d) {
     switch (d.grid) {
         case GSQ_GRID_INT2: return d.mk / GridT<GSQ_GRID_INT2>::N;
+        case GSQ_GRID_INT3: return d.mk / GridT<GSQ_GRID_INT3>::N;
         case GSQ_GRID_TERNARY: return d.mk / GridT<GSQ_GRID_TERNARY>::N;
         default: return d.mk / GridT<GSQ_GRID_INT3_LOCAL>::N;
     }
@@ -530,6 +537,7 @@ hipError_t launch_relax_fwd(const LayerDesc& d, const float* logits, const float
     }
     switch (d.grid) {
         case GSQ_GRID_INT2: GSQ_FWD_G(GSQ_GRID_INT2); break;
+        case GSQ_GRID_INT3: GSQ_FWD_G(GSQ_GRID_INT3); break;
         case GSQ_GRID_TERNARY: GSQ_FWD_G(GSQ_GRID_TERNARY); break;
         default: GSQ_FWD_G(GSQ_GRID_INT3_LOCAL); break;
     }
@@ -557,6 +565,7 @@ hipError_t launch_relax_bwd_lion(const LayerDesc& d, const float* G, float* logi
     else { GSQ_BWD_O(G_, false, true, false); }
     switch (d.grid) {
         case GSQ_GRID_INT2: GSQ_BWD_G(GSQ_GRID_INT2); break;
+        case GSQ_GRID_INT3: GSQ_BWD_G(GSQ_GRID_INT3); break;
         case GSQ_GRID_TERNARY: GSQ_BWD_G(GSQ_GRID_TERNARY); break;
         default: GSQ_BWD_G(GSQ_GRID_INT3_LOCAL); break;
     }
@@ -573,6 +582,9 @@ hipError_t launch_harden_pack(const LayerDesc& d, const float* logits, const flo
     switch (d.grid) {
         case GSQ_GRID_INT2:
             GSQ_LAUNCH((harden_pack_kernel<GSQ_GRID_INT2>), nb, st, logits, scales, codes, d.mk, codes_out, packed, scales_f16);
+            break;
+        case GSQ_GRID_INT3:
+            GSQ_LAUNCH((harden_pack_kernel<GSQ_GRID_INT3>), nb, st, logits, scales, codes, d.mk, codes_out, packed, scales_f16);
             break;
         case GSQ_GRID_TERNARY:
             GSQ_LAUNCH((harden_pack_kernel<GSQ_GRID_TERNARY>), nb, st, logits, scales, codes, d.mk, codes_out, packed, scales_f16);

@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-INT2, TERNARY, INT3_LOCAL = 0, 1, 2
+INT2, TERNARY, INT3_LOCAL, INT3 = 0, 1, 2, 3
 
 
 @dataclass(frozen=True)
@@ -54,6 +54,9 @@ WORKLOADS = {
     # 70B-shaped gate_proj, 3-bit local shift around the warm-start code.
     "gateproj28672x8192_int3local": Workload("gateproj28672x8192_int3local", 28672, 8192, 8192,
                                              INT3_LOCAL, 0.01, True, "normal"),
+    # The same gate_proj with the full 3-bit grid (8 logits): the baseline local shift replaces.
+    "gateproj28672x8192_int3full": Workload("gateproj28672x8192_int3full", 28672, 8192, 8192,
+                                            INT3, 0.01, True, "normal"),
     # 64 experts of 2048x7168, 2-bit, routed token counts ~ Zipf(1.1) on [64, 1024].
     "moe64x2048x7168_int2": Workload("moe64x2048x7168_int2", 64 * 2048, 7168, 20_900, INT2, 0.02,
                                      True, "normal", experts=64, rows_per_expert=2048,

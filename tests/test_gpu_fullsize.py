@@ -16,7 +16,7 @@ from tests.gpu_util import device, to_dev_bf16, bf16_values, f32, bf16_ulp, repo
 pytestmark = pytest.mark.gpu
 
 WORKLOADS = ["linear512_int2", "qproj4096_int2", "downproj4096x14336_ternary",
-             "gateproj28672x8192_int3local", "moe64x2048x7168_int2"]
+             "gateproj28672x8192_int3local", "gateproj28672x8192_int3full", "moe64x2048x7168_int2"]
 
 
 def _sample_rows(M, rpe, seed=0):

@@ -16,7 +16,7 @@ from tests.gpu_util import device, to_dev_bf16, bf16_values, f32, bf16_ulp, repo
 
 pytestmark = pytest.mark.gpu
 
-GRIDS = [oracle.GRID_INT2, oracle.GRID_TERNARY, oracle.GRID_INT3_LOCAL]
+GRIDS = [oracle.GRID_INT2, oracle.GRID_TERNARY, oracle.GRID_INT3_LOCAL, oracle.GRID_INT3]
 SHAPES = [(64, 512), (5, 384)]          # several scale groups per row; ragged row count
 
 # Soft weights and logit gradients: 1e-5 of their natural scale (s * q_max,
@@ -361,7 +361,7 @@ def test_harden_pack_bit_exact(dev, grid):
     lg[:, 0, :8] = 0.0                                           # all-equal logits
     if grid == oracle.GRID_TERNARY:
         lg[0, 1, :4] = -0.0
-    c0 = rng.integers(0, 8 if grid == oracle.GRID_INT3_LOCAL else 4, (M, K)).astype(np.uint8)
+    c0 = rng.integers(0, 4 if grid == oracle.GRID_INT2 else 8, (M, K)).astype(np.uint8)
     s = (np.abs(rng.normal(0, 0.01, (M, K // 128))) + 1e-4).astype(np.float32)
     s[0, 0] = 1.0 + 2.0 ** -11                                   # fp16 tie
     layer = g.GsqLayer.make(grid, M, K, g.DTYPE_BF16)

@@ -16,7 +16,8 @@ from tests.gpu_util import device, to_dev_bf16, report
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("grid", [oracle.GRID_INT2, oracle.GRID_TERNARY, oracle.GRID_INT3_LOCAL])
+@pytest.mark.parametrize("grid", [oracle.GRID_INT2, oracle.GRID_TERNARY, oracle.GRID_INT3_LOCAL,
+                                  oracle.GRID_INT3])
 def test_trajectory_matches_oracle(grid):
     import torch
     import post_weight_quantization_philox_amd as g
@@ -100,3 +101,41 @@ def test_gram_mode_trajectory_matches_oracle():
     assert agree >= 0.999
     assert agree_modes >= 0.99
     assert moved > 0.001
+
+
+def test_local_shift_coverage_of_the_full_grid():
+    """How often the full 3-bit grid (8 logits) ends within +-2 of the
+    warm-start code, the window local shift searches, after a whole annealed
+    solve (200 steps, tau 1 -> 0.05) on a synthetic layer; and the hard
+    reconstruction error of both against the round-to-nearest start (the
+    pages report the +-2 window holding almost every full-grid choice on real
+    layers, agihunt.info method paragraph). Logit lr 5e-2 so that codes move
+    within 200 steps; scale lr 1e-6: Lion moves a scale by lr every step
+    whatever its size, and the 3-bit scales (absmax / 7, about 0.007 here)
+    drift too far at 1e-5."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver
+    dev = device()
+    M, K, N, T = 512, 1024, 1024, 200
+    d = synthetic.small_layer(M, K, N, seed=4, w_bf16=True)
+    W, X = d["W"], d["X"]
+    s0, c0, _ = oracle.init_rtn(W, oracle.GRID_INT3)
+    rtn = oracle.hard_loss(c0, s0, W, X, oracle.GRID_INT3)
+    out = {}
+    for grid in (oracle.GRID_INT3, oracle.GRID_INT3_LOCAL):
+        sol = LayerSolver(to_dev_bf16(d["W_bits"], dev), to_dev_bf16(d["X_bits"], dev), grid,
+                          seed=0, stream_id=9, lion=g.GsqLion.make(lr_logit=5e-2, lr_scale=1e-6))
+        _, (codes, _, _) = sol.solve(T, 1.0, 0.05)
+        codes = codes.cpu().numpy()
+        scales = sol.scales.cpu().numpy()
+        out[grid] = (codes, oracle.hard_loss(codes, scales, W, X, grid))
+    full = out[oracle.GRID_INT3][0].astype(np.int64)
+    within = np.mean(np.abs(full - c0.astype(np.int64)) <= 2)
+    moved = np.mean(full != c0)
+    report("local-shift coverage", within_pm2=float(within), full_grid_moved=float(moved),
+           hard_loss_rtn=rtn, hard_loss_full=out[oracle.GRID_INT3][1],
+           hard_loss_local=out[oracle.GRID_INT3_LOCAL][1])
+    assert moved > 0.01                  # the solve moved codes, so the window is exercised
+    assert within >= 0.99
+    assert out[oracle.GRID_INT3][1] < rtn and out[oracle.GRID_INT3_LOCAL][1] < rtn
