@@ -131,29 +131,90 @@ def init_rtn(W, grid: int, group: int = 128, init_logit: float = 2.0):
     qmax = np.float32(Q_MAX[grid])
     amax = np.abs(w).reshape(M, K // group, group).max(axis=2)
     s = (amax / qmax).astype(np.float32)
-    s_full = np.repeat(s, group, axis=1)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        x = np.where(s_full > 0, w / np.where(s_full > 0, s_full, np.float32(1)),
-                     np.float32(0)).astype(np.float32)
-    L = N_LOGITS[grid]
-    logits = np.zeros((L, M, K), dtype=np.float32)
-    il = np.float32(init_logit)
-    if grid == GRID_TERNARY:
-        t0 = np.clip(np.rint(x), -1, 1).astype(np.int64)
-        codes = (t0 + 1).astype(np.uint8)
-        logits[0] = np.where(t0 != 0, il, -il)
-        logits[1] = np.where(w >= 0, il, -il)
-    else:
-        bits = CODE_BITS[grid]
-        u = ((x + qmax).astype(np.float32) * np.float32(0.5)).astype(np.float32)
-        c0 = np.clip(np.rint(u), 0, 2 ** bits - 1).astype(np.int64)
-        codes = c0.astype(np.uint8)
-        if grid in (GRID_INT2, GRID_INT3):
-            for k in range(L):
-                logits[k] = np.where(c0 == k, il, np.float32(0))
-        else:
-            logits[2] = il
+    codes, _ = _nearest_code(w, np.repeat(s, group, axis=1), grid)
+    codes = codes.astype(np.uint8)
+    logits = _logits_from_codes(codes, w, grid, init_logit)
     return s, codes, logits
+
+
+def _logits_from_codes(codes, W, grid: int, init_logit: float):
+    """Initial logits of warm-start codes, as :func:`init_rtn` sets them."""
+    c = np.asarray(codes, dtype=np.int64)
+    L = N_LOGITS[grid]
+    il = np.float32(init_logit)
+    logits = np.zeros((L,) + c.shape, dtype=np.float32)
+    if grid == GRID_TERNARY:
+        logits[0] = np.where(c != 1, il, -il)
+        logits[1] = np.where(np.asarray(W, dtype=np.float32) >= 0, il, -il)
+    elif grid == GRID_INT3_LOCAL:
+        logits[2] = il
+    else:
+        for k in range(L):
+            logits[k] = np.where(c == k, il, np.float32(0))
+    return logits
+
+
+def _nearest_code(t, s, grid: int):
+    """Round-to-nearest code of target values t (fp64) with scales s, decided
+    in fp32 exactly like :func:`init_rtn`: x = fp32(t) / s, then rint."""
+    qmax = np.float32(Q_MAX[grid])
+    tf = np.asarray(t, dtype=np.float64).astype(np.float32)
+    sf = np.asarray(s, dtype=np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        x = np.where(sf > 0, tf / np.where(sf > 0, sf, np.float32(1)), np.float32(0)).astype(np.float32)
+    if grid == GRID_TERNARY:
+        return (np.clip(np.rint(x), -1, 1).astype(np.int64) + 1), x
+    u = ((x + qmax).astype(np.float32) * np.float32(0.5)).astype(np.float32)
+    return np.clip(np.rint(u), 0, 2 ** CODE_BITS[grid] - 1).astype(np.int64), u
+
+
+def gptq_hessian(X, damp: float = 0.01) -> np.ndarray:
+    """H = X^T X with GPTQ's damping: lambda = damp * mean(diag H) added to the
+    diagonal; a column no token touches (zero diagonal) gets 1 there first,
+    so the factorisations exist (its weight does not change the objective)."""
+    Xd = np.asarray(X, dtype=np.float64)
+    H = Xd.T @ Xd
+    d = np.diag(H).copy()
+    d[d == 0] = 1.0
+    H[np.diag_indices_from(H)] = d
+    H[np.diag_indices_from(H)] += damp * float(np.mean(d))
+    return H
+
+
+def gptq(W, X, grid: int, group: int = 128, damp: float = 0.01, init_logit: float = 2.0):
+    """GPTQ warm start (Frantar, Ashkboos, Hoefler, Alistarh, "GPTQ: Accurate
+    Post-Training Quantization for Generative Pre-trained Transformers", 2022:
+    the Cholesky form of its column loop) on the symmetric group grid.
+
+    The pages start GSQ from GPTQ (agihunt.info optimizer paragraph;
+    atlas.scime.ai Approach). Group scales are the absmax scales of the
+    original weights (GPTQ's static-groups option), so they equal
+    :func:`init_rtn`'s. Then, column by column in order: the current column is
+    rounded to the nearest grid level (decided in fp32 as in init_rtn); its
+    error divided by the diagonal of the upper Cholesky factor U of H^-1
+    (H from :func:`gptq_hessian`) is fed into every later column through row
+    j of U. Returns ``(scales, codes, logits, targets)`` where targets [M, K]
+    are the fp64 values each column was rounded from.
+    """
+    w = np.array(W, dtype=np.float64)
+    M, K = w.shape
+    scales, _, _ = init_rtn(W, grid, group, init_logit)
+    s_full = np.repeat(scales, group, axis=1)
+    H = gptq_hessian(X, damp)
+    U = np.linalg.cholesky(np.linalg.inv(H)).T          # H^-1 = U^T U, U upper
+    codes = np.zeros((M, K), dtype=np.int64)
+    targets = np.zeros((M, K))
+    for j in range(K):
+        targets[:, j] = w[:, j]
+        c, _ = _nearest_code(w[:, j], s_full[:, j], grid)
+        codes[:, j] = c
+        v = (c - 1).astype(np.float64) if grid == GRID_TERNARY else \
+            level_value(c, CODE_BITS[grid]).astype(np.float64)
+        q = s_full[:, j].astype(np.float64) * v
+        err = (w[:, j] - q) / U[j, j]
+        w[:, j + 1:] -= np.outer(err, U[j, j + 1:])
+    codes = codes.astype(np.uint8)
+    return scales, codes, _logits_from_codes(codes, W, grid, init_logit), targets
 
 
 # ----------------------------------------------------------------------------
