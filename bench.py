@@ -151,6 +151,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the oracle sample (default: about 1.4e11 flops of products)")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--init", choices=("rtn", "gptq"), default="rtn",
+                    help="warm start; GPTQ's set-up time is reported under 'setup' (not in the step)")
     ap.add_argument("--unfused", action="store_true",
                     help="time separate forward and backward calls instead of the fused pass")
     ap.add_argument("--no-variants", action="store_true",
@@ -180,8 +182,13 @@ def main():
         Wd = torch.from_numpy(data["W"]).to(dev)
     Xd = torch.from_numpy(data["X_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
     lion = g.GsqLion.make(lr_logit=wl.lr_logit, lr_scale=1e-5)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter()
     solver = LayerSolver(Wd, Xd, wl.grid, tok_offsets=data["tok_offsets"],
-                         rows_per_expert=wl.rows_per_expert or None, seed=0, stream_id=0, lion=lion)
+                         rows_per_expert=wl.rows_per_expert or None, seed=0, stream_id=0, lion=lion,
+                         init=args.init)
+    torch.cuda.synchronize()
+    setup_ms = (time.perf_counter() - t_setup) * 1e3
     M, K, N = solver.rows, solver.cols, solver.tokens
     coords = M * K
     bpc = bytes_per_coord(wl.grid, wl.w_bf16)
@@ -281,6 +288,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "last_loss": loss,
+        "setup": {"init": args.init, "ms": setup_ms,
+                  "note": "warm start, X^T and state allocation, once per layer, not in the step"},
     }
     if not args.no_variants and not args.unfused and wl.experts == 1:
         # Same step with the objective in Gram form (H = X^T X formed once,

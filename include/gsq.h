@@ -133,6 +133,33 @@ gsq_status gsq_init_rtn(const gsq_layer* layer, const void* W, float* scales,
                         uint8_t* codes, float* logits, float init_logit,
                         void* stream);
 
+/* Workspace bytes of gsq_init_gptq for a layer of rows x cols: the fp32 Gram
+ * matrix, one fp64 cols x cols factor, fp64 rounding errors of the whole
+ * layer and one 128-column block of feedback (about 12*cols^2 + 8*rows*cols
+ * bytes). 0 for invalid sizes. */
+size_t gsq_gptq_workspace_bytes(int64_t rows, int64_t cols);
+
+/* GPTQ warm start (Frantar et al. 2022), the initialisation the pages start
+ * from (agihunt.info optimizer paragraph; atlas.scime.ai Approach), in place
+ * of gsq_init_rtn: the same absmax group scales (GPTQ's static groups), then
+ * codes chosen column by column with every rounding error fed into the later
+ * columns through H = X^T X + damp * mean(diag H) * I (a zero diagonal entry
+ * counts as 1), and logits set from the codes as gsq_init_rtn sets them.
+ *   W          [rows][cols] in layer->w_dtype
+ *   tokens     calibration tokens T (> 0, multiple of 64; zero rows pad)
+ *   XT         [cols][T] bf16 (gsq_transpose_tokens with one expert)
+ *   damp       >= 0 (GPTQ uses 0.01)
+ *   workspace  device scratch of at least gsq_gptq_workspace_bytes()
+ *   scales, codes, logits  out, as gsq_init_rtn
+ *   info       out device int32: 0, or j+1 when the damped Gram matrix was
+ *              not positive definite at (reversed) column j; read it after the
+ *              stream has finished. */
+gsq_status gsq_init_gptq(const gsq_layer* layer, const void* W, int64_t tokens,
+                         const uint16_t* XT, float damp, float init_logit,
+                         void* workspace, size_t workspace_bytes, float* scales,
+                         uint8_t* codes, float* logits, int32_t* info,
+                         void* stream);
+
 /* Relaxed forward (agihunt.info method paragraph: soft weighted sum of grid
  * points). With noise n_k drawn for `step` and eta = noise_scale:
  *   2-bit / local shift: p = softmax((l + eta*g)/tau), g standard Gumbel,

@@ -17,6 +17,7 @@ __all__ = [
     "GRID_INT2", "GRID_TERNARY", "GRID_INT3_LOCAL", "GRID_INT3", "DTYPE_F32", "DTYPE_BF16",
     "GsqError", "GsqLayer", "GsqLion", "lib", "exported_symbols",
     "gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
+    "gsq_gptq_workspace_bytes", "gsq_init_gptq",
     "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
     "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes", "gsq_recon_gram",
     "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd", "gsq_harden_pack", "gsq_noise_dump",
@@ -31,6 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsq.so")
 
 #: Entry points declared in include/gsq.h.
 EXPORTS = ("gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
+           "gsq_gptq_workspace_bytes", "gsq_init_gptq",
            "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
            "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes",
            "gsq_recon_gram", "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd",
@@ -89,6 +91,9 @@ def lib() -> ctypes.CDLL:
         "gsq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "gsq_num_logits": (ctypes.c_int, [ctypes.c_int]),
         "gsq_init_rtn": (st, [_L, _P, _P, _P, _P, ctypes.c_float, _P]),
+        "gsq_gptq_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
+        "gsq_init_gptq": (st, [_L, _P, ctypes.c_int64, _P, ctypes.c_float, ctypes.c_float, _P,
+                               ctypes.c_size_t, _P, _P, _P, _P, _P]),
         "gsq_relax_fwd": (st, [_L, _P, _P, _P, _P, ctypes.c_uint32, ctypes.c_float,
                                ctypes.c_float, _P, _P, _P]),
         "gsq_recon_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, _P, ctypes.c_int64,
@@ -176,6 +181,20 @@ def gsq_init_rtn(layer: GsqLayer, W, scales, codes, logits, init_logit: float = 
     _check("gsq_init_rtn", lib().gsq_init_rtn(ctypes.byref(layer), _ptr(W), _ptr(scales),
                                               _ptr(codes), _ptr(logits), init_logit,
                                               _stream(stream)))
+
+
+def gsq_gptq_workspace_bytes(rows: int, cols: int) -> int:
+    return lib().gsq_gptq_workspace_bytes(rows, cols)
+
+
+def gsq_init_gptq(layer: GsqLayer, W, tokens: int, XT, damp: float, init_logit: float, workspace,
+                  scales, codes, logits, info, stream=None, workspace_bytes=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("gsq_init_gptq",
+           lib().gsq_init_gptq(ctypes.byref(layer), _ptr(W), tokens, _ptr(XT), damp, init_logit,
+                               _ptr(workspace), workspace_bytes, _ptr(scales), _ptr(codes),
+                               _ptr(logits), _ptr(info), _stream(stream)))
 
 
 def gsq_relax_fwd(layer: GsqLayer, logits, scales, init_codes, W, step: int, tau: float,

@@ -100,6 +100,12 @@ gsq_status check_offsets(int32_t n_experts, const int64_t* offs, int64_t rows_pe
     return GSQ_OK;
 }
 
+// The GEMM addresses each bf16 operand with 32-bit byte offsets below 2^31
+// (plus the contraction length), so an operand must stay under about 2 GiB.
+inline bool gemm_operand_fits(int64_t rows, int64_t ld, int64_t contraction) {
+    return rows * ld * 2 <= int64_t(0x7FFFFF00) - 2 * contraction;
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,6 +138,40 @@ gsq_status gsq_init_rtn(const gsq_layer* layer, const void* W, float* scales, ui
     if (!std::isfinite(init_logit)) return GSQ_ERR_PARAM;
     return hip_status(gsq::launch_init_rtn(d, W, scales, codes, logits, init_logit,
                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t gsq_gptq_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || rows > INT32_MAX || cols <= 0 || (cols % 128) != 0 || cols > INT32_MAX) return 0;
+    if (rows > kMaxCoords / cols || cols > kMaxCoords / cols) return 0;
+    return gsq::gptq_workspace_bytes(rows, cols);
+}
+
+gsq_status gsq_init_gptq(const gsq_layer* layer, const void* W, int64_t tokens, const uint16_t* XT,
+                         float damp, float init_logit, void* workspace, size_t workspace_bytes,
+                         float* scales, uint8_t* codes, float* logits, int32_t* info,
+                         void* stream) {
+    LayerDesc d;
+    GSQ_TRY(check_layer(layer, &d));
+    GSQ_TRY(need(W));
+    GSQ_TRY(need(XT));
+    GSQ_TRY(need(workspace));
+    GSQ_TRY(need(scales));
+    GSQ_TRY(need(codes));
+    GSQ_TRY(need(logits));
+    if (info == nullptr) return GSQ_ERR_NULL;
+    if (tokens <= 0 || (tokens % 64) != 0 || tokens > INT32_MAX) return GSQ_ERR_SHAPE;
+    if (tokens > kMaxCoords / d.cols) return GSQ_ERR_SHAPE;
+    if (!gemm_operand_fits(d.cols, tokens, tokens)) return GSQ_ERR_SHAPE;
+    if (!(damp >= 0.0f) || !std::isfinite(damp) || !std::isfinite(init_logit)) return GSQ_ERR_PARAM;
+    if (workspace_bytes < gsq_gptq_workspace_bytes(d.rows, d.cols)) return GSQ_ERR_SHAPE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    gsq::GptqWorkspace ws = gsq::gptq_carve(workspace, d.rows, d.cols);
+    ws.scales = scales;
+    hipError_t err = gsq::launch_init_rtn(d, W, scales, codes, logits, init_logit, st);
+    if (err == hipSuccess) err = gsq::launch_gram_f32(tokens, d.cols, XT, ws.H32, st);
+    if (err == hipSuccess) err = gsq::launch_gptq_factor(d.cols, damp, ws, info, st);
+    if (err == hipSuccess) err = gsq::launch_gptq_columns(d, W, ws, codes, logits, init_logit, st);
+    return hip_status(err);
 }
 
 gsq_status gsq_relax_fwd(const gsq_layer* layer, const float* logits, const float* scales,
@@ -192,12 +232,6 @@ gsq_status gsq_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets, i
     GSQ_TRY(need(XT));
     return hip_status(gsq::launch_transpose_tokens(n_experts, tok_offsets, cols, X, XT,
                                                    static_cast<hipStream_t>(stream)));
-}
-
-// The GEMM addresses each bf16 operand with 32-bit byte offsets below 2^31
-// (plus the contraction length), so an operand must stay under about 2 GiB.
-inline bool gemm_operand_fits(int64_t rows, int64_t ld, int64_t contraction) {
-    return rows * ld * 2 <= int64_t(0x7FFFFF00) - 2 * contraction;
 }
 
 gsq_status gsq_gram(int64_t tokens, int64_t cols, const uint16_t* XT, uint16_t* H, void* stream) {

@@ -579,6 +579,13 @@ hipError_t launch_gram(int64_t tokens, int64_t cols, const uint16_t* XT, uint16_
                               static_cast<int>(tokens), H, cols, 1.0f, nullptr, st);
 }
 
+hipError_t launch_gram_f32(int64_t tokens, int64_t cols, const uint16_t* XT, float* H32,
+                           hipStream_t st) {
+    return run_gemm<EPI_F32_SCALED>(XT, tokens, XT, tokens, static_cast<int>(cols),
+                                    static_cast<int>(cols), static_cast<int>(tokens), H32, cols, 1.0f,
+                                    nullptr, st);
+}
+
 hipError_t launch_recon_gram(int64_t rows, int64_t cols, const uint16_t* H, const uint16_t* dW,
                              float* partials, float* G, double* loss, hipStream_t st) {
     // C = dW H^T = dW H (H is symmetric); G = 2 C; loss = sum dW * C.

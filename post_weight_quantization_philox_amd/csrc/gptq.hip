@@ -1,0 +1,408 @@
+// GPTQ warm start on the GPU (Frantar, Ashkboos, Hoefler, Alistarh, "GPTQ:
+// Accurate Post-Training Quantization for Generative Pre-trained
+// Transformers", 2022), the initialisation the pages start GSQ from
+// (agihunt.info optimizer paragraph; atlas.scime.ai Approach).
+//
+// GPTQ rounds the columns of W in order and feeds every rounding error into
+// the later columns through the upper Cholesky factor of H^-1. The same
+// recursion can be written on a factor of H itself, with no inverse: if
+// H = R R^T with R upper triangular, column j is rounded from
+//     t_j = w_j + sum_{i<j} (w_i - q_i) R_ij / R_jj
+// (Babai's nearest-plane recursion; equal to GPTQ's column loop in exact
+// arithmetic). R is the lower Cholesky factor of H with its index order
+// reversed: R = J chol(J H J) J, J the reversal. Everything here is fp64
+// except the rounding decision, which is taken in fp32 exactly like the
+// round-to-nearest warm start (x = fp32(t) / s).
+//
+// Steps: H = X^T X (fp32, matrix cores, gemm.hip); lambda = damp * mean
+// diag(H) (a zero diagonal entry counts as 1); A = J (H + lambda I) J in fp64
+// (lower triangle); blocked right-looking Cholesky of A in place (32-column
+// panels: the diagonal block in LDS, a triangular solve for the rows below,
+// a symmetric rank-32 update of the trailing lower triangle); then
+// V_ij = R_ij / R_jj for i < j, written into the unused upper triangle of A;
+// then for every 128-column group: P = D[:, <j0] V[<j0, group] (fp64 tiled
+// product of the earlier columns' errors D = W - Q), and one thread per row
+// runs the 128 columns of the group sequentially with the group's block of V
+// and the row's errors in LDS. Group scales are the absmax scales of the
+// original weights (GPTQ's static groups), i.e. the round-to-nearest scales.
+#include <math.h>
+
+#include "gsq_internal.hpp"
+
+namespace gsq {
+
+namespace {
+
+constexpr int kPanel = 32;     // Cholesky panel width
+constexpr int kBlock = 128;    // GPTQ column block = scale group
+
+template <int GRID> struct GT;
+template <> struct GT<GSQ_GRID_INT2> { static constexpr int L = 4, QMAX = 3, BITS = 2; };
+template <> struct GT<GSQ_GRID_TERNARY> { static constexpr int L = 2, QMAX = 1, BITS = 2; };
+template <> struct GT<GSQ_GRID_INT3_LOCAL> { static constexpr int L = 5, QMAX = 7, BITS = 3; };
+template <> struct GT<GSQ_GRID_INT3> { static constexpr int L = 8, QMAX = 7, BITS = 3; };
+
+__global__ void zero_info_kernel(int32_t* info) { *info = 0; }
+
+// lambda = damp * mean(diag H), a zero diagonal entry counted as 1. One
+// workgroup; fixed-order sums, so the value is deterministic.
+__global__ __launch_bounds__(256) void damping_kernel(const float* __restrict__ H32, int64_t K,
+                                                      float damp, double* __restrict__ lambda) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < K; i += 256) {
+        const double d = static_cast<double>(H32[i * K + i]);
+        s += (d == 0.0) ? 1.0 : d;
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *lambda = static_cast<double>(damp) * (red[0] / static_cast<double>(K));
+}
+
+// A[i][j] = H[K-1-i][K-1-j] (+ lambda on the diagonal, zero diagonals set to
+// 1 first) for j <= i. 2-D grid of 16x16 threads.
+__global__ __launch_bounds__(256) void reverse_damp_kernel(const float* __restrict__ H32, int64_t K,
+                                                           const double* __restrict__ lambda,
+                                                           double* __restrict__ A) {
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x & 15);
+    const int64_t i = static_cast<int64_t>(blockIdx.y) * 16 + (threadIdx.x >> 4);
+    if (i >= K || j >= K || j > i) return;
+    double v = static_cast<double>(H32[(K - 1 - i) * K + (K - 1 - j)]);
+    if (i == j) v = ((v == 0.0) ? 1.0 : v) + *lambda;
+    A[i * K + j] = v;
+}
+
+// Cholesky of the kPanel x kPanel diagonal block at (p, p), in LDS. A pivot
+// that is not positive records its 1-based column in *info (first failure
+// only) and is replaced by 1 so the rest stays finite.
+__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ A, int64_t K, int64_t p,
+                                                         int32_t* __restrict__ info) {
+    __shared__ double t[kPanel][kPanel + 1];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < kPanel * kPanel; e += 256) {
+        const int i = e / kPanel, j = e % kPanel;
+        t[i][j] = (j <= i) ? A[(p + i) * K + p + j] : 0.0;
+    }
+    __syncthreads();
+    for (int k = 0; k < kPanel; ++k) {
+        if (tid == 0) {
+            double d = t[k][k];
+            if (!(d > 0.0)) {
+                if (*info == 0) *info = static_cast<int32_t>(p + k + 1);
+                d = 1.0;
+            }
+            t[k][k] = sqrt(d);
+        }
+        __syncthreads();
+        if (tid > k && tid < kPanel) t[tid][k] /= t[k][k];
+        __syncthreads();
+        for (int e = tid; e < kPanel * kPanel; e += 256) {
+            const int i = e / kPanel, j = e % kPanel;
+            if (j > k && i >= j) t[i][j] -= t[i][k] * t[j][k];
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < kPanel * kPanel; e += 256) {
+        const int i = e / kPanel, j = e % kPanel;
+        if (j <= i) A[(p + i) * K + p + j] = t[i][j];
+    }
+}
+
+// Rows below the panel: x L11^T = a, one thread per row.
+__global__ __launch_bounds__(256) void trsm_kernel(double* __restrict__ A, int64_t K, int64_t p) {
+    __shared__ double L[kPanel][kPanel + 1];
+    for (int e = threadIdx.x; e < kPanel * kPanel; e += 256) {
+        const int i = e / kPanel, j = e % kPanel;
+        L[i][j] = (j <= i) ? A[(p + i) * K + p + j] : 0.0;
+    }
+    __syncthreads();
+    const int64_t i = p + kPanel + static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= K) return;
+    double x[kPanel];
+#pragma unroll
+    for (int k = 0; k < kPanel; ++k) x[k] = A[i * K + p + k];
+#pragma unroll
+    for (int k = 0; k < kPanel; ++k) {
+        double v = x[k];
+#pragma unroll
+        for (int m = 0; m < k; ++m) v -= x[m] * L[k][m];
+        x[k] = v / L[k][k];
+    }
+#pragma unroll
+    for (int k = 0; k < kPanel; ++k) A[i * K + p + k] = x[k];
+}
+
+// Trailing update A22 -= L21 L21^T on the lower triangle, 64x64 tiles
+// enumerated over the lower triangle of tiles; 4x4 outputs per thread.
+__global__ __launch_bounds__(256) void syrk_kernel(double* __restrict__ A, int64_t K, int64_t p) {
+    __shared__ double Pi[64][kPanel + 1];
+    __shared__ double Pj[64][kPanel + 1];
+    const int64_t q = p + kPanel;
+    const int64_t x = blockIdx.x;
+    int64_t bi = static_cast<int64_t>((sqrt(8.0 * static_cast<double>(x) + 1.0) - 1.0) * 0.5);
+    while (bi * (bi + 1) / 2 > x) --bi;
+    while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
+    const int64_t bj = x - bi * (bi + 1) / 2;
+    const int64_t r0 = q + bi * 64, c0 = q + bj * 64;
+    for (int e = threadIdx.x; e < 64 * kPanel; e += 256) {
+        const int r = e / kPanel, k = e % kPanel;
+        Pi[r][k] = (r0 + r < K) ? A[(r0 + r) * K + p + k] : 0.0;
+        Pj[r][k] = (c0 + r < K) ? A[(c0 + r) * K + p + k] : 0.0;
+    }
+    __syncthreads();
+    const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+    double acc[4][4] = {};
+#pragma unroll 4
+    for (int k = 0; k < kPanel; ++k) {
+        double a[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { a[u] = Pi[ty * 4 + u][k]; b[u] = Pj[tx * 4 + u][k]; }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t row = r0 + ty * 4 + u;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t col = c0 + tx * 4 + v;
+            if (row < K && col <= row) A[row * K + col] -= acc[u][v];
+        }
+    }
+}
+
+// V_ij = R_ij / R_jj (i < j) into the upper triangle of A, where
+// R_ij = L[K-1-i][K-1-j] (strictly lower part of A) and R_jj its diagonal.
+__global__ __launch_bounds__(256) void make_v_kernel(double* __restrict__ A, int64_t K) {
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x & 15);
+    const int64_t i = static_cast<int64_t>(blockIdx.y) * 16 + (threadIdx.x >> 4);
+    if (i >= K || j >= K || i >= j) return;
+    const int64_t ri = K - 1 - i, rj = K - 1 - j;
+    A[i * K + j] = A[ri * K + rj] / A[rj * K + rj];
+}
+
+// P[c][r] = sum_{i < j0} Dt[i][r] V[i][j0 + c] for c < kBlock, r < M (both
+// column-major over r). 64x64 output tiles, 4x4 per thread, contraction in
+// chunks of 16 staged through LDS.
+__global__ __launch_bounds__(256) void gptq_gemm_kernel(const double* __restrict__ Dt,
+                                                        const double* __restrict__ A, int64_t K,
+                                                        int64_t M, int64_t j0, double* __restrict__ P) {
+    __shared__ double sD[16][64 + 1];
+    __shared__ double sV[16][64 + 1];
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
+    const int c0 = blockIdx.y * 64;
+    const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+    double acc[4][4] = {};
+    for (int64_t k0 = 0; k0 < j0; k0 += 16) {
+        for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+            const int k = e >> 6, c = e & 63;
+            sD[k][c] = (r0 + c < M) ? Dt[(k0 + k) * M + r0 + c] : 0.0;
+            sV[k][c] = A[(k0 + k) * K + j0 + c0 + c];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            double a[4], b[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { a[u] = sD[k][ty * 4 + u]; b[u] = sV[k][tx * 4 + u]; }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t r = r0 + ty * 4 + u;
+        if (r >= M) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) P[static_cast<int64_t>(c0 + tx * 4 + v) * M + r] = acc[u][v];
+    }
+}
+
+// Level value of a code in scale units (ternary codes are t + 1).
+template <int GRID>
+__device__ __forceinline__ double level_of(int code) {
+    if constexpr (GRID == GSQ_GRID_TERNARY) return static_cast<double>(code - 1);
+    else return static_cast<double>(2 * code - ((1 << GT<GRID>::BITS) - 1));
+}
+
+// Nearest code of target t with scale s, decided in fp32 like the
+// round-to-nearest warm start: x = fp32(t) / s, u = (x + q_max) / 2, rint.
+template <int GRID>
+__device__ __forceinline__ int nearest_code(double t, float s) {
+    constexpr float qmax = static_cast<float>(GT<GRID>::QMAX);
+    const float x = (s > 0.0f) ? __fdiv_rn(static_cast<float>(t), s) : 0.0f;
+    if constexpr (GRID == GSQ_GRID_TERNARY) {
+        return static_cast<int>(fminf(fmaxf(rintf(x), -1.0f), 1.0f)) + 1;
+    } else {
+        constexpr float cmax = static_cast<float>((1 << GT<GRID>::BITS) - 1);
+        const float u = __fmul_rn(__fadd_rn(x, qmax), 0.5f);
+        return static_cast<int>(fminf(fmaxf(rintf(u), 0.0f), cmax));
+    }
+}
+
+// One 128-column group: one thread per row (64 rows per workgroup) rounds
+// the columns in order from t_j = w_j + P_j + sum_{i<j in group} d_i V_ij.
+// The group's strictly upper block of V (packed, 8128 doubles) and the
+// workgroup's errors d (128 x 64 doubles) sit in LDS.
+template <int GRID, bool WBF16>
+__global__ __launch_bounds__(64) void gptq_block_kernel(const void* __restrict__ W, int64_t M,
+                                                        int64_t K, int64_t j0,
+                                                        const double* __restrict__ A,
+                                                        const double* __restrict__ P, int has_p,
+                                                        const float* __restrict__ scales,
+                                                        double* __restrict__ Dt,
+                                                        uint8_t* __restrict__ codes) {
+    __shared__ double Vp[kBlock * (kBlock - 1) / 2];
+    __shared__ double dl[kBlock][64];
+    const int lane = threadIdx.x;
+    for (int j = 1; j < kBlock; ++j)
+        for (int i = lane; i < j; i += 64) Vp[j * (j - 1) / 2 + i] = A[(j0 + i) * K + j0 + j];
+    __syncthreads();
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+    if (r >= M) return;
+    const float s = scales[r * (K / kBlock) + j0 / kBlock];
+    uint32_t packed[kBlock / 4];
+#pragma unroll
+    for (int q = 0; q < kBlock / 4; ++q) packed[q] = 0;
+#pragma unroll 1
+    for (int j = 0; j < kBlock; ++j) {
+        double w;
+        if constexpr (WBF16) w = static_cast<double>(bf16_lo(static_cast<const uint16_t*>(W)[r * K + j0 + j]));
+        else w = static_cast<double>(static_cast<const float*>(W)[r * K + j0 + j]);
+        double t = w;
+        if (has_p) t += P[static_cast<int64_t>(j) * M + r];
+        const double* vj = Vp + j * (j - 1) / 2;
+        for (int i = 0; i < j; ++i) t = fma(dl[i][lane], vj[i], t);
+        const int code = nearest_code<GRID>(t, s);
+        const double d = w - static_cast<double>(s) * level_of<GRID>(code);
+        dl[j][lane] = d;
+        Dt[(j0 + j) * M + r] = d;
+        // Register index known only at run time: select through a switch-free
+        // shift into the word the unrolled store loop below writes.
+#pragma unroll
+        for (int q = 0; q < kBlock / 4; ++q)
+            if (q == (j >> 2)) packed[q] |= static_cast<uint32_t>(code) << (8 * (j & 3));
+    }
+    uint4* dst = reinterpret_cast<uint4*>(codes + r * K + j0);
+#pragma unroll
+    for (int q = 0; q < kBlock / 16; ++q)
+        dst[q] = make_uint4(packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]);
+}
+
+// Initial logits of the GPTQ codes (as the round-to-nearest warm start sets
+// them): +init_logit on the code's level, 0 elsewhere; local shift: offset 0
+// (index 2); ternary: mask +-init_logit by t != 0, sign by the sign of w.
+template <int GRID, bool WBF16>
+__global__ __launch_bounds__(256) void codes_to_logits_kernel(const uint8_t* __restrict__ codes,
+                                                              const void* __restrict__ W, uint64_t mk,
+                                                              float init_logit,
+                                                              float* __restrict__ logits) {
+    constexpr int L = GT<GRID>::L;
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= mk) return;
+    const int c = codes[i];
+    if constexpr (GRID == GSQ_GRID_TERNARY) {
+        float w;
+        if constexpr (WBF16) w = bf16_lo(static_cast<const uint16_t*>(W)[i]);
+        else w = static_cast<const float*>(W)[i];
+        logits[i] = (c != 1) ? init_logit : -init_logit;
+        logits[mk + i] = (w >= 0.0f) ? init_logit : -init_logit;
+    } else if constexpr (GRID == GSQ_GRID_INT3_LOCAL) {
+#pragma unroll
+        for (int k = 0; k < L; ++k) logits[k * mk + i] = (k == 2) ? init_logit : 0.0f;
+    } else {
+#pragma unroll
+        for (int k = 0; k < L; ++k) logits[k * mk + i] = (k == c) ? init_logit : 0.0f;
+    }
+}
+
+inline unsigned cdivu(int64_t a, int64_t b) { return static_cast<unsigned>((a + b - 1) / b); }
+
+template <int GRID, bool WBF16>
+hipError_t gptq_columns(const LayerDesc& d, const void* W, const GptqWorkspace& ws, uint8_t* codes,
+                        float* logits, float init_logit, hipStream_t st) {
+    const int64_t M = d.rows, K = d.cols;
+    for (int64_t j0 = 0; j0 < K; j0 += kBlock) {
+        if (j0 > 0) {
+            hipLaunchKernelGGL(gptq_gemm_kernel, dim3(cdivu(M, 64), kBlock / 64), dim3(256), 0, st,
+                               ws.Dt, ws.A, K, M, j0, ws.P);
+        }
+        hipLaunchKernelGGL((gptq_block_kernel<GRID, WBF16>), dim3(cdivu(M, 64)), dim3(64), 0, st, W,
+                           M, K, j0, ws.A, ws.P, j0 > 0 ? 1 : 0, ws.scales, ws.Dt, codes);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL((codes_to_logits_kernel<GRID, WBF16>), dim3(cdivu(d.mk, 256)), dim3(256), 0,
+                       st, codes, W, d.mk, init_logit, logits);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gptq_workspace_bytes(int64_t rows, int64_t cols) {
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t K = static_cast<size_t>(cols), M = static_cast<size_t>(rows);
+    return al(K * K * sizeof(float)) + al(K * K * sizeof(double)) + al(M * K * sizeof(double)) +
+           al(M * kBlock * sizeof(double)) + al(sizeof(double));
+}
+
+GptqWorkspace gptq_carve(void* base, int64_t rows, int64_t cols) {
+    auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t K = static_cast<size_t>(cols), M = static_cast<size_t>(rows);
+    char* p = static_cast<char*>(base);
+    GptqWorkspace ws{};
+    ws.H32 = reinterpret_cast<float*>(p);  p += al(K * K * sizeof(float));
+    ws.A = reinterpret_cast<double*>(p);   p += al(K * K * sizeof(double));
+    ws.Dt = reinterpret_cast<double*>(p);  p += al(M * K * sizeof(double));
+    ws.P = reinterpret_cast<double*>(p);   p += al(M * kBlock * sizeof(double));
+    ws.lambda = reinterpret_cast<double*>(p);
+    return ws;
+}
+
+hipError_t launch_gptq_factor(int64_t cols, float damp, const GptqWorkspace& ws, int32_t* info,
+                              hipStream_t st) {
+    const int64_t K = cols;
+    hipLaunchKernelGGL(zero_info_kernel, dim3(1), dim3(1), 0, st, info);
+    hipLaunchKernelGGL(damping_kernel, dim3(1), dim3(256), 0, st, ws.H32, K, damp, ws.lambda);
+    hipLaunchKernelGGL(reverse_damp_kernel, dim3(cdivu(K, 16), cdivu(K, 16)), dim3(256), 0, st,
+                       ws.H32, K, ws.lambda, ws.A);
+    for (int64_t p = 0; p < K; p += kPanel) {
+        hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, st, ws.A, K, p, info);
+        const int64_t rest = K - p - kPanel;
+        if (rest > 0) {
+            hipLaunchKernelGGL(trsm_kernel, dim3(cdivu(rest, 256)), dim3(256), 0, st, ws.A, K, p);
+            const int64_t T = (rest + 63) / 64;
+            hipLaunchKernelGGL(syrk_kernel, dim3(static_cast<unsigned>(T * (T + 1) / 2)), dim3(256), 0,
+                               st, ws.A, K, p);
+        }
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(make_v_kernel, dim3(cdivu(K, 16), cdivu(K, 16)), dim3(256), 0, st, ws.A, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_gptq_columns(const LayerDesc& d, const void* W, const GptqWorkspace& ws,
+                               uint8_t* codes, float* logits, float init_logit, hipStream_t st) {
+#define GSQ_GPTQ(G)                                                                         \
+    return d.w_bf16 ? gptq_columns<G, true>(d, W, ws, codes, logits, init_logit, st)        \
+                    : gptq_columns<G, false>(d, W, ws, codes, logits, init_logit, st);
+    switch (d.grid) {
+        case GSQ_GRID_INT2: GSQ_GPTQ(GSQ_GRID_INT2)
+        case GSQ_GRID_TERNARY: GSQ_GPTQ(GSQ_GRID_TERNARY)
+        case GSQ_GRID_INT3_LOCAL: GSQ_GPTQ(GSQ_GRID_INT3_LOCAL)
+        default: GSQ_GPTQ(GSQ_GRID_INT3)
+    }
+#undef GSQ_GPTQ
+}
+
+}  // namespace gsq

@@ -54,6 +54,26 @@ hipError_t launch_gram(int64_t tokens, int64_t cols, const uint16_t* XT, uint16_
                        hipStream_t st);
 hipError_t launch_recon_gram(int64_t rows, int64_t cols, const uint16_t* H, const uint16_t* dW,
                              float* partials, float* G, double* loss, hipStream_t st);
+// H = X^T X in fp32 (GPTQ's Hessian), [cols][cols].
+hipError_t launch_gram_f32(int64_t tokens, int64_t cols, const uint16_t* XT, float* H32,
+                           hipStream_t st);
+
+// GPTQ warm start (gptq.hip): scratch carved from one caller-provided buffer.
+struct GptqWorkspace {
+    float* H32;           // [cols][cols] X^T X
+    double* A;            // [cols][cols]: reversed Cholesky factor (lower), V (upper)
+    double* Dt;           // [cols][rows] rounding errors, column-major
+    double* P;            // [128][rows] feedback from earlier groups, column-major
+    double* lambda;       // damping added to the diagonal
+    const float* scales;  // [rows][cols/128] group scales (the caller's output)
+};
+size_t gptq_workspace_bytes(int64_t rows, int64_t cols);
+GptqWorkspace gptq_carve(void* base, int64_t rows, int64_t cols);
+hipError_t launch_gptq_factor(int64_t cols, float damp, const GptqWorkspace& ws, int32_t* info,
+                              hipStream_t st);
+hipError_t launch_gptq_columns(const LayerDesc& d, const void* W, const GptqWorkspace& ws,
+                               uint8_t* codes, float* logits, float init_logit, hipStream_t st);
+
 hipError_t launch_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets, int64_t cols,
                                    const uint16_t* X, uint16_t* XT, hipStream_t st);
 

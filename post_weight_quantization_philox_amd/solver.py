@@ -24,7 +24,7 @@ import numpy as np
 import torch
 
 from . import (GRID_INT3_LOCAL, DTYPE_BF16, DTYPE_F32, N_LOGITS, CODE_BITS, GsqLayer,
-               GsqLion, gsq_init_rtn, gsq_relax_fwd, gsq_recon_workspace_bytes,
+               GsqLion, gsq_init_rtn, gsq_gptq_workspace_bytes, gsq_init_gptq, gsq_relax_fwd, gsq_recon_workspace_bytes,
                gsq_recon_loss_grad, gsq_transpose_tokens, gsq_gram,
                gsq_recon_gram_workspace_bytes, gsq_recon_gram, gsq_relax_bwd_lion,
                gsq_relax_bwd_lion_fwd, gsq_harden_pack)
@@ -63,7 +63,7 @@ class LayerSolver:
     def __init__(self, W: torch.Tensor, X: torch.Tensor, grid: int, tok_offsets=None,
                  rows_per_expert: int | None = None, seed: int = 0, stream_id: int = 0,
                  lion: GsqLion | None = None, init_logit: float = 2.0,
-                 recon: str = "direct"):
+                 recon: str = "direct", init: str = "rtn", damp: float = 0.01):
         if not (W.is_cuda and X.is_cuda):
             raise ValueError("W and X must be device tensors")
         if W.dtype not in (torch.bfloat16, torch.float32) or X.dtype != torch.bfloat16:
@@ -111,8 +111,21 @@ class LayerSolver:
             ws = gsq_recon_workspace_bytes(self.n_experts, self.tok_offsets, self.rows_per_expert, K)
         self.workspace = torch.empty((max(ws, 256) // 4,), **f32)
         self.loss = torch.zeros((1,), dtype=torch.float64, device=dev)
-        gsq_init_rtn(self.layer, self.W, self.scales, self.codes, self.logits, init_logit)
+        if init not in ("rtn", "gptq"):
+            raise ValueError("init must be 'rtn' or 'gptq'")
+        if init == "gptq" and (self.n_experts != 1 or self.tokens == 0):
+            raise ValueError("the GPTQ warm start is for one dense layer with tokens")
         gsq_transpose_tokens(self.n_experts, self.tok_offsets, K, self.X, self.XT)
+        self.gptq_info = None
+        if init == "gptq":
+            ws = torch.empty((gsq_gptq_workspace_bytes(M, K) + 255) // 256 * 256,
+                             dtype=torch.uint8, device=dev)
+            self.gptq_info = torch.zeros((1,), dtype=torch.int32, device=dev)
+            gsq_init_gptq(self.layer, self.W, self.tokens, self.XT, damp, init_logit, ws,
+                          self.scales, self.codes, self.logits, self.gptq_info)
+            del ws
+        else:
+            gsq_init_rtn(self.layer, self.W, self.scales, self.codes, self.logits, init_logit)
         if recon == "gram":
             if self.tokens == 0:
                 self.H.zero_()

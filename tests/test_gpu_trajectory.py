@@ -139,3 +139,44 @@ def test_local_shift_coverage_of_the_full_grid():
     assert moved > 0.01                  # the solve moved codes, so the window is exercised
     assert within >= 0.99
     assert out[oracle.GRID_INT3][1] < rtn and out[oracle.GRID_INT3_LOCAL][1] < rtn
+
+
+def test_trajectory_from_gptq_start():
+    """GSQ started from the GPU's GPTQ warm start, against the oracle's step
+    loop started from the same state (codes, scales and logits copied)."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver, tau_schedule
+    dev = device()
+    grid = oracle.GRID_INT3_LOCAL
+    M, K, N, T = 256, 512, 512, 24
+    d = synthetic.small_layer(M, K, N, seed=3, w_bf16=True)
+    lr_logit, lr_scale = 5e-2, 1e-6
+    solver = LayerSolver(to_dev_bf16(d["W_bits"], dev), to_dev_bf16(d["X_bits"], dev), grid,
+                         seed=0, stream_id=4, init="gptq",
+                         lion=g.GsqLion.make(lr_logit=lr_logit, lr_scale=lr_scale))
+    torch.cuda.synchronize()
+    assert int(solver.gptq_info.item()) == 0
+    c0 = solver.codes.cpu().numpy()
+    state = {"logits": solver.logits.cpu().numpy(), "mom": np.zeros((5, M, K), np.float32),
+             "scales": solver.scales.cpu().numpy(), "scale_mom": np.zeros((M, K // 128), np.float32),
+             "codes": c0}
+    taus = tau_schedule(T, 1.0, 0.1)
+    solver.relax_fwd(0, taus[0])
+    gpu_losses = []
+    for t in range(T):
+        solver.step_fused(t, taus[t], taus[t + 1] if t + 1 < T else None)
+        gpu_losses.append(float(solver.loss.item()))
+    codes = solver.harden()[0].cpu().numpy()
+    ref = [oracle.step(state, d["W"], d["X"], grid, t, taus[t], 0, 4, lr_logit, lr_scale,
+                       bf16_dW=True, bf16_RT=True) for t in range(T)]
+    c_ref = oracle.harden(state["logits"], grid, c0)
+    rel = np.abs(np.array(gpu_losses) - ref) / np.array(ref)
+    agree = np.mean(codes == c_ref)
+    s_rtn, c_rtn, _ = oracle.init_rtn(d["W"], grid)
+    report("trajectory from gptq", max_rel_loss=float(rel.max()), code_agreement=float(agree),
+           hard_rtn=oracle.hard_loss(c_rtn, s_rtn, d["W"], d["X"], grid),
+           hard_gptq=oracle.hard_loss(c0, s_rtn, d["W"], d["X"], grid),
+           hard_after=oracle.hard_loss(c_ref, state["scales"], d["W"], d["X"], grid))
+    assert rel.max() <= 2e-3
+    assert agree >= 0.999
