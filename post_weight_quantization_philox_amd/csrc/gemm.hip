@@ -140,7 +140,7 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const uint32
     for (int q = 0; q < 8; ++q) {
         const int r0 = 8 * (4 * q + wave);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + r0 * kChunks), 16,
-                                                 off[q] + koff, 0, 0, 0);
+                                                 off[q], koff, 0, 0);
     }
 }
 
@@ -171,7 +171,9 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     const int i0 = ti * BM, j0 = tj * BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // Wave index as a scalar: LDS destinations of the DMA loads (the M0
+    // operand) then come from scalar arithmetic.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wi = wave >> 1, wj = wave & 1;
 
     // Per-lane byte offsets of the rows this lane fetches. Rows past the edge
@@ -223,10 +225,10 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
         const int r0 = 8 * (4 * q + wave);
         if (d < 8)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rs, (lds_void*)(nA + r0 * kChunks), 16,
-                                                     oa[q] + koff, 0, 0, 0);
+                                                     oa[q], koff, 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rs, (lds_void*)(nB + r0 * kChunks), 16,
-                                                     ob[q] + koff, 0, 0, 0);
+                                                     ob[q], koff, 0, 0);
     };
     // Two of the eight fragment reads of slice kk into its slot, in the
     // order its MFMAs consume them: B blocks 0-1, B 2-3, A 0-1, A 2-3.
