@@ -115,12 +115,30 @@ def describe(wl) -> str:
     return f"{wl.rows}x{wl.cols} {w}, {grid}, group 128, {wl.tokens} tokens bf16 {x}"
 
 
+SPIN_UP_S = 0.5
+
+
+def spin_up(step_fn):
+    """Untimed steps for SPIN_UP_S seconds of wall time before the warm-up
+    steps: the GPU's clocks take longer than a few milliseconds of work to
+    settle, and the timed steps should see the steady state."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SPIN_UP_S:
+        for _ in range(10):
+            step_fn()
+        torch.cuda.synchronize()
+
+
 def time_fused(solver, taus, warmup: int, steps: int, stream):
     """Fused-step timing loop: returns (elapsed s, mean recon ms, mean fused
     backward+forward ms). Step t = objective of step t (dW from the previous
     pass) + backward and Lion of step t fused with the forward of step t + 1."""
     import numpy as np
     import torch
+    solver.relax_fwd(0, taus[0])
+    spin_up(lambda: solver.step_fused(0, taus[0], taus[1]))
     solver.relax_fwd(0, taus[0])
     for t in range(warmup):
         solver.step_fused(t, taus[t], taus[t + 1])
@@ -208,6 +226,7 @@ def main():
     offs = [int(o) for o in solver.tok_offsets]
     n_gemm = 2 * max(1, sum(1 for e in range(len(offs) - 1) if offs[e + 1] > offs[e]))
     if args.unfused:
+        spin_up(lambda: solver.step(0, taus[0]))
         for t in range(args.warmup):
             solver.step(t, taus[t])
         torch.cuda.synchronize()
