@@ -111,6 +111,45 @@ def test_recon_validation(L):
     assert g.gsq_recon_workspace_bytes(1, offs_bad, 64, 256) == 0
 
 
+def test_gram_validation(L):
+    gr = g.lib().gsq_gram
+    assert gr(100, 256, FAKE, FAKE, None) == ERR_SHAPE                 # tokens not a multiple of 64
+    assert gr(128, 200, FAKE, FAKE, None) == ERR_SHAPE                 # cols not a multiple of 128
+    assert gr(128, 256, None, FAKE, None) == ERR_NULL
+    assert gr(128, 256, FAKE, FAKE_MISALIGNED, None) == ERR_ALIGN
+    assert gr(64, (1 << 20) + 128, FAKE, FAKE, None) == ERR_SHAPE      # cols^2 > 2^40 coordinates
+    rg = g.lib().gsq_recon_gram
+    ws = g.gsq_recon_gram_workspace_bytes(300, 256)
+    assert ws >= 4 and ws % 256 == 0
+    assert g.gsq_recon_gram_workspace_bytes(300, 100) == 0
+    assert rg(0, 256, FAKE, FAKE, FAKE, ws, FAKE, FAKE, None) == ERR_SHAPE
+    assert rg(300, 256, None, FAKE, FAKE, ws, FAKE, FAKE, None) == ERR_NULL
+    assert rg(300, 256, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == ERR_SHAPE
+    assert rg(300, 256, FAKE, FAKE, FAKE, ws, FAKE_MISALIGNED, FAKE, None) == ERR_ALIGN
+    assert rg(1 << 21, 1 << 10, FAKE, FAKE, FAKE, ws, FAKE, FAKE, None) == ERR_SHAPE   # dW over 2 GiB
+
+
+def test_gptq_validation(L):
+    lay = g.GsqLayer.make(g.GRID_INT2, 64, 256)
+    f = g.lib().gsq_init_gptq
+    ws = g.gsq_gptq_workspace_bytes(64, 256)
+    assert ws >= 256 * 256 * 12 + 64 * 256 * 8
+    assert g.gsq_gptq_workspace_bytes(64, 100) == 0
+    args = lambda **k: [ctypes.byref(k.get("lay", lay)), k.get("W", FAKE), k.get("tokens", 128),
+                        k.get("XT", FAKE), ctypes.c_float(k.get("damp", 0.01)), ctypes.c_float(2.0),
+                        k.get("ws", FAKE), k.get("nbytes", ws), FAKE, FAKE, FAKE,
+                        k.get("info", FAKE), None]
+    assert f(*args(tokens=100)) == ERR_SHAPE
+    assert f(*args(tokens=0)) == ERR_SHAPE
+    assert f(*args(damp=-0.5)) == ERR_PARAM
+    assert f(*args(damp=float("nan"))) == ERR_PARAM
+    assert f(*args(nbytes=16)) == ERR_SHAPE
+    assert f(*args(XT=None)) == ERR_NULL
+    assert f(*args(info=None)) == ERR_NULL
+    assert f(*args(W=FAKE_MISALIGNED)) == ERR_ALIGN
+    assert f(*args(lay=g.GsqLayer.make(7, 64, 256))) == ERR_GRID
+
+
 def test_harden_and_noise_validation(L):
     lay = g.GsqLayer.make(g.GRID_INT3_LOCAL, 4, 256)
     h = g.lib().gsq_harden_pack

@@ -232,3 +232,71 @@ def test_fullsize_gram(name):
     rel = abs(loss_gram - loss_direct) / loss_direct
     report(f"{name} gram", loss_gram=loss_gram, loss_direct=loss_direct, rel=rel)
     assert rel <= 4e-3
+
+
+def test_beyond_32bit_offsets():
+    """A 2-bit layer of 33000 x 32768 (1.08e9 coordinates, past 2^30): the
+    relax kernels switch to 64-bit element offsets, and the Philox counters
+    of the last rows pass 2^32 (stream element i*L). The relaxed forward and
+    the fused backward + Lion + next forward on sampled rows against the
+    oracle. Inputs are drawn on the device from a seeded generator; the
+    sampled rows are copied back."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    dev = device()
+    grid, L = oracle.GRID_INT2, 4
+    M, K = 33000, 32768
+    assert M * K > 2 ** 30 and (M - 1) * K * L > 2 ** 32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    W = (torch.randn((M, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    layer = g.GsqLayer.make(grid, M, K, g.DTYPE_BF16, seed=5, stream=1)
+    scales = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    codes = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    logits = torch.empty((L, M, K), dtype=torch.float32, device=dev)
+    g.gsq_init_rtn(layer, W, scales, codes, logits, 2.0)
+    logits.add_(torch.randn((L, M, K), generator=gen, device=dev))
+    rows = [0, 16383, 32767, 32768, M - 1]
+    Wr = bf16_values(W[rows]).astype(np.float32)
+    l0 = f32(logits[:, rows])
+    s0 = f32(scales[rows])
+    dW = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    g.gsq_relax_fwd(layer, logits, scales, None, W, 3, 0.5, 1.0, dW)
+    torch.cuda.synchronize()
+    dWr = bf16_values(dW[rows]).astype(np.float64)
+    for j, r in enumerate(rows):
+        ref = oracle.relax_fwd(l0[:, j:j + 1], s0[j:j + 1], Wr[j:j + 1], grid, 5, 1, 3, 0.5, 1.0,
+                               row0=r)
+        nat = np.repeat(s0[j].astype(np.float64), 128) * 3
+        assert np.all(np.abs(dWr[j] - ref["dW"][0]) <= bf16_ulp(ref["dW"][0]) + 1e-5 * nat)
+    _log("beyond 2^30: relax_fwd ok")
+    del dW
+    G = torch.randn((M, K), generator=gen, device=dev) * 1e3
+    mom = torch.zeros((L, M, K), dtype=torch.float32, device=dev)
+    smom = torch.zeros((M, K // 128), dtype=torch.float32, device=dev)
+    Gr = f32(G[rows]).astype(np.float64)
+    lion = g.GsqLion.make(lr_logit=1e-3, lr_scale=1e-5)
+    dW2 = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    g.gsq_relax_bwd_lion_fwd(layer, G, logits, mom, scales, smom, None, W, 3, 0.5, 1.0, lion, 4,
+                             0.45, dW2)
+    torch.cuda.synchronize()
+    l1, s1 = f32(logits[:, rows]), f32(scales[rows])
+    dW2r = bf16_values(dW2[rows]).astype(np.float64)
+    for j, r in enumerate(rows):
+        gl, gs = oracle.relax_bwd(Gr[j:j + 1], l0[:, j:j + 1], s0[j:j + 1], grid, 5, 1, 3, 0.5, 1.0,
+                                  row0=r)
+        th, mm = oracle.lion(l0[:, j:j + 1], gl, np.zeros_like(l0[:, j:j + 1]), 1e-3, 0.9, 0.99)
+        nat = np.abs(Gr[j]) * np.repeat(s0[j].astype(np.float64), 128) * 3 / 0.5
+        # Lion's sign may differ only where the gradient is within its tolerance of 0
+        differ = l1[:, j] != th[:, 0]
+        assert np.all(np.abs(gl[:, 0][differ]) <= 1e-5 * np.broadcast_to(nat, gl[:, 0].shape)[differ])
+        assert differ.mean() < 1e-3
+        ref = oracle.relax_fwd(l1[:, j:j + 1], s1[j:j + 1], Wr[j:j + 1], grid, 5, 1, 4, 0.45, 1.0,
+                               row0=r)
+        nat2 = np.repeat(s1[j].astype(np.float64), 128) * 3
+        assert np.all(np.abs(dW2r[j] - ref["dW"][0]) <= bf16_ulp(ref["dW"][0]) + 1e-5 * nat2)
+        gsum_tol = 130 * 2.0 ** -24 * (np.abs(Gr[j]) * 3).reshape(-1, 128).sum(1) + 1e-30
+        sn, _ = oracle.lion(s0[j:j + 1], gs, np.zeros_like(s0[j:j + 1]), 1e-5, 0.9, 0.99)
+        flips = s1[j] != sn[0]
+        assert np.all(np.abs(gs[0][flips]) <= gsum_tol[flips])
+    _log("beyond 2^30: fused backward + Lion + next forward ok")
