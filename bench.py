@@ -330,6 +330,23 @@ def main():
             "last_loss": float(gsol.loss.item()),
         }}
         del gsol
+        # The same annealed steps captured as one HIP graph (launch overhead
+        # removed; it matters for small layers), timed over one replay.
+        torch.cuda.empty_cache()
+        csol = LayerSolver(Wd, Xd, wl.grid, seed=0, stream_id=0, lion=lion)
+        graph = csol.capture_solve(args.steps)
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_el = (time.perf_counter() - t0) / 3
+        out["variants"]["graph"] = {
+            "value": coords * args.steps / g_el, "unit": "weights/s",
+            "ms_per_step": g_el * 1e3 / args.steps,
+            "note": "the two-product step, whole K-step solve replayed as one HIP graph"}
+        del csol, graph
     if not args.no_cpu_baseline and wl.experts == 1:
         rows = args.cpu_rows or max(64, min(M, int(4096 * 4096 * 4096 // (K * N)) // 64 * 64))
         out["cpu_baseline"] = cpu_baseline(data, rows)

@@ -140,13 +140,15 @@ class LayerSolver:
         gsq_relax_fwd(self.layer, self.logits, self.scales, self.init_codes, self.W, step, tau,
                       noise_scale, self.dW, w_soft_dbg)
 
-    def recon(self):
+    def recon(self, loss_out=None):
+        """Objective and gradient of the current dW; the loss goes to
+        ``loss_out`` (a 16-byte aligned device fp64 scalar) or ``self.loss``."""
+        loss = self.loss if loss_out is None else loss_out
         if self.recon_mode == "gram":
-            gsq_recon_gram(self.rows, self.cols, self.H, self.dW, self.workspace, self.G, self.loss)
+            gsq_recon_gram(self.rows, self.cols, self.H, self.dW, self.workspace, self.G, loss)
         else:
             gsq_recon_loss_grad(self.n_experts, self.tok_offsets, self.rows_per_expert, self.cols,
-                                self.X, self.XT, self.dW, self.workspace, self.RT, self.G,
-                                self.loss)
+                                self.X, self.XT, self.dW, self.workspace, self.RT, self.G, loss)
 
     def relax_bwd_lion(self, step: int, tau: float, noise_scale: float = 1.0,
                        grad_logits_dbg=None, grad_scales_dbg=None):
@@ -176,6 +178,28 @@ class LayerSolver:
             self.relax_bwd_lion(step, tau, noise_scale)
         else:
             self.relax_bwd_lion_fwd(step, tau, step + 1, next_tau, noise_scale)
+
+    def capture_solve(self, steps: int, tau0: float = 1.0, tau1: float = 0.05,
+                      noise_scale: float = 1.0):
+        """The whole annealed solve (first forward, then every step's
+        objective and fused backward + Lion + next forward) captured as one
+        HIP graph, so a replay launches it with one call instead of about four
+        launches per step. Temperatures are fixed at capture; the loss of step
+        t lands in ``self.loss_hist[t, 0]``. Replaying continues from the
+        current state (it does not reset it). Returns the graph."""
+        taus = tau_schedule(steps, tau0, tau1)
+        # one 16-byte slot per step (device tensors are passed 16-byte aligned)
+        self.loss_hist = torch.zeros((steps, 2), dtype=torch.float64, device=self.W.device)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.relax_fwd(0, taus[0], noise_scale)
+            for t, tau in enumerate(taus):
+                self.recon(self.loss_hist[t])
+                if t + 1 < steps:
+                    self.relax_bwd_lion_fwd(t, tau, t + 1, taus[t + 1], noise_scale)
+                else:
+                    self.relax_bwd_lion(t, tau, noise_scale)
+        return graph
 
     def harden(self):
         """Hard codes (uint8), packed codes (int32 words) and fp16 scales."""
