@@ -160,6 +160,43 @@ def time_fused(solver, taus, warmup: int, steps: int, stream):
     return elapsed, rec_ms, fus_ms
 
 
+def block_bench(args, dev):
+    """GSQ's staged schedule (query/key, value/output, MLP) over one decoder
+    block of Llama-3.1-8B shape with seeded random weights and 4096 tokens of
+    N(0,1) activations: weights/s = all projection weights x steps per layer /
+    wall time of the whole schedule (forwards, set-up, solves, hardening)."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.block import LLAMA3_8B, staged_quantize
+    cfg = LLAMA3_8B
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    w = {}
+    for name, (o, i) in cfg.shapes().items():
+        w[name] = (torch.randn((o, i), generator=gen, device=dev) / i ** 0.5).to(torch.bfloat16)
+    w["g_attn"] = torch.ones(cfg.hidden, device=dev)
+    w["g_mlp"] = torch.ones(cfg.hidden, device=dev)
+    x = torch.randn((4096, cfg.hidden), generator=gen, device=dev).to(torch.bfloat16)
+    lion = g.GsqLion.make(lr_logit=1e-3, lr_scale=1e-5)
+    staged_quantize(cfg, w, x[:256], g.GRID_INT2, 2, lion)      # warm the code paths
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, info = staged_quantize(cfg, w, x, g.GRID_INT2, args.block_steps, lion)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    n_w = sum(o * i for o, i in cfg.shapes().values())
+    print(json.dumps({
+        "metric": "GSQ staged block schedule weights/sec (all projections x steps)",
+        "value": n_w * args.block_steps / el, "unit": "weights/s", "n_gpus": 1,
+        "steps": args.block_steps, "seconds": el, "higher_is_better": True, "data": "synthetic",
+        "dtype": "f32 relax+Lion, bf16 MFMA (fp32 accumulate), bf16 block forward",
+        "config": {"workload": "Llama-3.1-8B-shaped decoder block (hidden 4096, 32 heads, 8 kv "
+                               "heads, MLP 14336), random weights, 4096 tokens N(0,1), 2-bit grid",
+                   "weights": n_w},
+        "stages": {k: {"seconds": v["seconds"]} for k, v in info.items()},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +206,10 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the oracle sample (default: about 1.4e11 flops of products)")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--block", action="store_true",
+                    help="time GSQ's staged schedule over one Llama-3.1-8B-shaped decoder block "
+                         "(random weights, 4096 tokens) instead of the per-layer step")
+    ap.add_argument("--block-steps", type=int, default=50)
     ap.add_argument("--init", choices=("rtn", "gptq"), default="rtn",
                     help="warm start; GPTQ's set-up time is reported under 'setup' (not in the step)")
     ap.add_argument("--unfused", action="store_true",
@@ -192,6 +233,9 @@ def main():
         sys.exit(1)
     g.lib()
     dev = torch.device("cuda:0")
+    if args.block:
+        block_bench(args, dev)
+        return
     data = synthetic.generate(args.workload, seed=0)
     wl = data["workload"]
     if wl.w_bf16:

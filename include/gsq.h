@@ -160,6 +160,46 @@ gsq_status gsq_init_gptq(const gsq_layer* layer, const void* W, int64_t tokens,
                          uint8_t* codes, float* logits, int32_t* info,
                          void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Block forward pieces for the staged schedule: the pages optimise a decoder
+ * block in stages (query/key, then value/output, then the MLP on the block
+ * output), each stage's calibration inputs computed from the block with the
+ * earlier stages quantized and frozen (agihunt.info optimizer paragraph).
+ * bf16 tensors in and out, fp32 arithmetic, row-major; device pointers owned
+ * by the caller, 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+
+/* C[i][j] = sum_r A[i][r] B[j][r] (bf16 operands, fp32 accumulation, bf16
+ * result, round to nearest even). Rd a multiple of 64; lda, ldb >= Rd and
+ * ldc >= J, all leading dimensions and J multiples of 8 elements. */
+gsq_status gsq_matmul_nt_bf16(int64_t I, int64_t J, int64_t Rd, const uint16_t* A,
+                              int64_t lda, const uint16_t* B, int64_t ldb,
+                              uint16_t* C, int64_t ldc, void* stream);
+
+/* y = x / sqrt(mean_j x^2 + eps) * gamma per row; x, y [rows][cols] bf16,
+ * gamma [cols] fp32, eps > 0. */
+gsq_status gsq_rmsnorm_bf16(int64_t rows, int64_t cols, const uint16_t* x,
+                            const float* gamma, float eps, uint16_t* y, void* stream);
+
+/* P[i][j] = softmax over j <= i of scale * S[i][j] (causal), 0 for j > i;
+ * S, P [n][n] bf16. */
+gsq_status gsq_softmax_causal_bf16(int64_t n, const uint16_t* S, float scale,
+                                   uint16_t* P, void* stream);
+
+/* act = silu(gate) * up elementwise (SwiGLU), n elements. */
+gsq_status gsq_silu_mul_bf16(int64_t n, const uint16_t* gate, const uint16_t* up,
+                             uint16_t* act, void* stream);
+
+/* out = a + b elementwise (residual), n elements. */
+gsq_status gsq_add_bf16(int64_t n, const uint16_t* a, const uint16_t* b,
+                        uint16_t* out, void* stream);
+
+/* Hard weights W = s * v(code) in bf16 from gsq_harden_pack's codes (uint8
+ * [rows][cols]) and fp16 scales ([rows][cols/128]); v as in gsq_harden_pack
+ * (ternary codes are t + 1; local-shift codes are final 3-bit codes). */
+gsq_status gsq_dequant_bf16(const gsq_layer* layer, const uint8_t* codes,
+                            const uint16_t* scales_f16, uint16_t* W, void* stream);
+
 /* Relaxed forward (agihunt.info method paragraph: soft weighted sum of grid
  * points). With noise n_k drawn for `step` and eta = noise_scale:
  *   2-bit / local shift: p = softmax((l + eta*g)/tau), g standard Gumbel,

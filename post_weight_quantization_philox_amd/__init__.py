@@ -17,7 +17,8 @@ __all__ = [
     "GRID_INT2", "GRID_TERNARY", "GRID_INT3_LOCAL", "GRID_INT3", "DTYPE_F32", "DTYPE_BF16",
     "GsqError", "GsqLayer", "GsqLion", "lib", "exported_symbols",
     "gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
-    "gsq_gptq_workspace_bytes", "gsq_init_gptq",
+    "gsq_gptq_workspace_bytes", "gsq_init_gptq", "gsq_matmul_nt_bf16", "gsq_rmsnorm_bf16",
+    "gsq_softmax_causal_bf16", "gsq_silu_mul_bf16", "gsq_add_bf16", "gsq_dequant_bf16",
     "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
     "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes", "gsq_recon_gram",
     "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd", "gsq_harden_pack", "gsq_noise_dump",
@@ -32,7 +33,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsq.so")
 
 #: Entry points declared in include/gsq.h.
 EXPORTS = ("gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
-           "gsq_gptq_workspace_bytes", "gsq_init_gptq",
+           "gsq_gptq_workspace_bytes", "gsq_init_gptq", "gsq_matmul_nt_bf16",
+           "gsq_rmsnorm_bf16", "gsq_softmax_causal_bf16", "gsq_silu_mul_bf16", "gsq_add_bf16",
+           "gsq_dequant_bf16",
            "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
            "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes",
            "gsq_recon_gram", "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd",
@@ -92,6 +95,13 @@ def lib() -> ctypes.CDLL:
         "gsq_num_logits": (ctypes.c_int, [ctypes.c_int]),
         "gsq_init_rtn": (st, [_L, _P, _P, _P, _P, ctypes.c_float, _P]),
         "gsq_gptq_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
+        "gsq_matmul_nt_bf16": (st, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P,
+                                    ctypes.c_int64, _P, ctypes.c_int64, _P, ctypes.c_int64, _P]),
+        "gsq_rmsnorm_bf16": (st, [ctypes.c_int64, ctypes.c_int64, _P, _P, ctypes.c_float, _P, _P]),
+        "gsq_softmax_causal_bf16": (st, [ctypes.c_int64, _P, ctypes.c_float, _P, _P]),
+        "gsq_silu_mul_bf16": (st, [ctypes.c_int64, _P, _P, _P, _P]),
+        "gsq_add_bf16": (st, [ctypes.c_int64, _P, _P, _P, _P]),
+        "gsq_dequant_bf16": (st, [_L, _P, _P, _P, _P]),
         "gsq_init_gptq": (st, [_L, _P, ctypes.c_int64, _P, ctypes.c_float, ctypes.c_float, _P,
                                ctypes.c_size_t, _P, _P, _P, _P, _P]),
         "gsq_relax_fwd": (st, [_L, _P, _P, _P, _P, ctypes.c_uint32, ctypes.c_float,
@@ -195,6 +205,36 @@ def gsq_init_gptq(layer: GsqLayer, W, tokens: int, XT, damp: float, init_logit: 
            lib().gsq_init_gptq(ctypes.byref(layer), _ptr(W), tokens, _ptr(XT), damp, init_logit,
                                _ptr(workspace), workspace_bytes, _ptr(scales), _ptr(codes),
                                _ptr(logits), _ptr(info), _stream(stream)))
+
+
+def gsq_matmul_nt_bf16(I: int, J: int, Rd: int, A, lda: int, B, ldb: int, C, ldc: int,
+                       stream=None):
+    _check("gsq_matmul_nt_bf16", lib().gsq_matmul_nt_bf16(I, J, Rd, _ptr(A), lda, _ptr(B), ldb,
+                                                          _ptr(C), ldc, _stream(stream)))
+
+
+def gsq_rmsnorm_bf16(rows: int, cols: int, x, gamma, eps: float, y, stream=None):
+    _check("gsq_rmsnorm_bf16", lib().gsq_rmsnorm_bf16(rows, cols, _ptr(x), _ptr(gamma), eps,
+                                                      _ptr(y), _stream(stream)))
+
+
+def gsq_softmax_causal_bf16(n: int, S, scale: float, P, stream=None):
+    _check("gsq_softmax_causal_bf16", lib().gsq_softmax_causal_bf16(n, _ptr(S), scale, _ptr(P),
+                                                                    _stream(stream)))
+
+
+def gsq_silu_mul_bf16(n: int, gate, up, act, stream=None):
+    _check("gsq_silu_mul_bf16", lib().gsq_silu_mul_bf16(n, _ptr(gate), _ptr(up), _ptr(act),
+                                                        _stream(stream)))
+
+
+def gsq_add_bf16(n: int, a, b, out, stream=None):
+    _check("gsq_add_bf16", lib().gsq_add_bf16(n, _ptr(a), _ptr(b), _ptr(out), _stream(stream)))
+
+
+def gsq_dequant_bf16(layer: GsqLayer, codes, scales_f16, W, stream=None):
+    _check("gsq_dequant_bf16", lib().gsq_dequant_bf16(ctypes.byref(layer), _ptr(codes),
+                                                      _ptr(scales_f16), _ptr(W), _stream(stream)))
 
 
 def gsq_relax_fwd(layer: GsqLayer, logits, scales, init_codes, W, step: int, tau: float,

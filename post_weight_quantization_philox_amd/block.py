@@ -1,0 +1,169 @@
+"""Staged GSQ over one decoder block, driven from the host.
+
+The pages optimise a transformer block in stages rather than all layers at
+once: the query and key projections first, then the value and output
+projections, then the MLP on the block's output. Each stage is frozen before
+the next, and its quantized weights shape the calibration inputs the later
+stages see (agihunt.info, optimizer paragraph). This module runs that
+schedule on a Llama-shaped decoder block (RMSNorm, causal attention with
+grouped key/value heads and no positional rotation, SwiGLU MLP, two
+residuals). Every step runs in ``libgsq.so``: the projections and attention
+products on the bf16 NT GEMM, normalisation, softmax, SwiGLU, residuals and
+dequantisation in their own kernels, and each layer's optimisation in
+:class:`~post_weight_quantization_philox_amd.solver.LayerSolver`.
+
+Readings: query and key are quantized together as one row-stacked layer (they
+see the same input); the value/output stage quantizes V, then O on the
+attention output recomputed with the quantized Q, K and V; gate and up are
+quantized together, then down on the SwiGLU activations recomputed with the
+quantized gate and up.
+"""
+
+from __future__ import annotations
+
+import math
+import time
+from dataclasses import dataclass
+
+import torch
+
+from . import (GsqLion, GsqLayer, DTYPE_BF16, gsq_matmul_nt_bf16, gsq_rmsnorm_bf16,
+               gsq_softmax_causal_bf16, gsq_silu_mul_bf16, gsq_add_bf16, gsq_dequant_bf16,
+               gsq_transpose_tokens)
+from .solver import LayerSolver
+
+PROJECTIONS = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+@dataclass(frozen=True)
+class BlockConfig:
+    hidden: int
+    heads: int
+    kv_heads: int
+    head_dim: int
+    mlp: int
+    eps: float = 1e-5
+
+    @property
+    def q_dim(self) -> int:
+        return self.heads * self.head_dim
+
+    @property
+    def kv_dim(self) -> int:
+        return self.kv_heads * self.head_dim
+
+    def shapes(self) -> dict:
+        """[out, in] of every projection."""
+        h = self.hidden
+        return {"q": (self.q_dim, h), "k": (self.kv_dim, h), "v": (self.kv_dim, h),
+                "o": (h, self.q_dim), "gate": (self.mlp, h), "up": (self.mlp, h),
+                "down": (h, self.mlp)}
+
+
+LLAMA3_8B = BlockConfig(hidden=4096, heads=32, kv_heads=8, head_dim=128, mlp=14336)
+
+
+def _bf16(shape, dev):
+    return torch.empty(shape, dtype=torch.bfloat16, device=dev)
+
+
+def _linear(x, W):
+    """x [n][in] times W [out][in]^T -> [n][out] (bf16)."""
+    n, k = x.shape
+    out = W.shape[0]
+    y = _bf16((n, out), x.device)
+    gsq_matmul_nt_bf16(n, out, k, x, k, W, k, y, out)
+    return y
+
+
+def forward(cfg: BlockConfig, w: dict, x: torch.Tensor) -> dict:
+    """The block on tokens x [n][hidden] (bf16) with weights ``w`` (bf16
+    projections [out][in], fp32 norm gains ``g_attn``, ``g_mlp``). Returns
+    the block output and the input each projection sees: ``x_attn`` (q, k,
+    v), ``x_o`` (o), ``x_mlp`` (gate, up), ``x_down`` (down); also ``h``,
+    the residual stream after attention."""
+    n, d = x.shape
+    dev = x.device
+    xa = _bf16((n, d), dev)
+    gsq_rmsnorm_bf16(n, d, x, w["g_attn"], cfg.eps, xa)
+    Q, K, V = _linear(xa, w["q"]), _linear(xa, w["k"]), _linear(xa, w["v"])
+    VT = _bf16((cfg.kv_dim * n,), dev)
+    gsq_transpose_tokens(1, [0, n], cfg.kv_dim, V, VT)
+    S = _bf16((n, n), dev)
+    P = _bf16((n, n), dev)
+    ao = _bf16((n, cfg.q_dim), dev)
+    group = cfg.heads // cfg.kv_heads
+    hd = cfg.head_dim
+    scale = 1.0 / math.sqrt(hd)
+    for h in range(cfg.heads):
+        g = h // group
+        gsq_matmul_nt_bf16(n, n, hd, Q[:, h * hd:], cfg.q_dim, K[:, g * hd:], cfg.kv_dim, S, n)
+        gsq_softmax_causal_bf16(n, S, scale, P)
+        gsq_matmul_nt_bf16(n, hd, n, P, n, VT[g * hd * n:], n, ao[:, h * hd:], cfg.q_dim)
+    hres = _bf16((n, d), dev)
+    gsq_add_bf16(n * d, x, _linear(ao, w["o"]), hres)
+    xm = _bf16((n, d), dev)
+    gsq_rmsnorm_bf16(n, d, hres, w["g_mlp"], cfg.eps, xm)
+    act = _bf16((n, cfg.mlp), dev)
+    gsq_silu_mul_bf16(n * cfg.mlp, _linear(xm, w["gate"]), _linear(xm, w["up"]), act)
+    out = _bf16((n, d), dev)
+    gsq_add_bf16(n * d, hres, _linear(act, w["down"]), out)
+    return {"out": out, "x_attn": xa, "x_o": ao, "h": hres, "x_mlp": xm, "x_down": act}
+
+
+def _quantize(W: torch.Tensor, X: torch.Tensor, grid: int, steps: int, lion: GsqLion,
+              tau0: float, tau1: float, init: str, seed: int, stream_id: int):
+    """One layer's annealed solve; returns the hard weights (bf16) and the
+    last relaxed loss."""
+    sol = LayerSolver(W, X, grid, seed=seed, stream_id=stream_id, lion=lion, init=init)
+    losses, (codes, _, s16) = sol.solve(steps, tau0, tau1, log_every=steps)
+    Wq = torch.empty_like(W)
+    layer = GsqLayer.make(grid, W.shape[0], W.shape[1], DTYPE_BF16)
+    gsq_dequant_bf16(layer, codes, s16.view(torch.int16), Wq)
+    return Wq, losses[-1]
+
+
+def staged_quantize(cfg: BlockConfig, w: dict, x: torch.Tensor, grid: int, steps: int,
+                    lion: GsqLion | None = None, tau0: float = 1.0, tau1: float = 0.05,
+                    init: str = "rtn", seed: int = 0):
+    """The staged schedule. Returns ``(wq, info)``: the weights with every
+    projection replaced by its hard quantized version, and per stage the wall
+    time, the calibration inputs used and the last relaxed loss."""
+    lion = lion or GsqLion.make()
+    wq = dict(w)
+    info = {}
+
+    def stage(name, fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = fn()
+        torch.cuda.synchronize()
+        info[name] = {"seconds": time.perf_counter() - t0, **out}
+
+    def s1():
+        xa = forward(cfg, wq, x)["x_attn"]
+        qk = torch.cat([w["q"], w["k"]], dim=0)
+        hq, loss = _quantize(qk, xa, grid, steps, lion, tau0, tau1, init, seed, 0)
+        wq["q"], wq["k"] = hq[:cfg.q_dim].contiguous(), hq[cfg.q_dim:].contiguous()
+        return {"x": xa, "loss": loss}
+
+    def s2():
+        xa = forward(cfg, wq, x)["x_attn"]
+        wq["v"], lv = _quantize(w["v"], xa, grid, steps, lion, tau0, tau1, init, seed, 1)
+        xo = forward(cfg, wq, x)["x_o"]
+        wq["o"], lo = _quantize(w["o"], xo, grid, steps, lion, tau0, tau1, init, seed, 2)
+        return {"x": xo, "loss": lv + lo}
+
+    def s3():
+        xm = forward(cfg, wq, x)["x_mlp"]
+        gu = torch.cat([w["gate"], w["up"]], dim=0)
+        hgu, lgu = _quantize(gu, xm, grid, steps, lion, tau0, tau1, init, seed, 3)
+        wq["gate"], wq["up"] = hgu[:cfg.mlp].contiguous(), hgu[cfg.mlp:].contiguous()
+        xd = forward(cfg, wq, x)["x_down"]
+        wq["down"], ld = _quantize(w["down"], xd, grid, steps, lion, tau0, tau1, init, seed, 4)
+        return {"x": xd, "loss": lgu + ld}
+
+    stage("q_k", s1)
+    stage("v_o", s2)
+    stage("mlp", s3)
+    return wq, info

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgsq.so")
-SOURCES = ["relax.hip", "gemm.hip", "gptq.hip", "abi.hip"]
+SOURCES = ["relax.hip", "gemm.hip", "gptq.hip", "block.hip", "abi.hip"]
 ARCH = os.environ.get("GSQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -174,6 +174,71 @@ gsq_status gsq_init_gptq(const gsq_layer* layer, const void* W, int64_t tokens, 
     return hip_status(err);
 }
 
+gsq_status gsq_matmul_nt_bf16(int64_t I, int64_t J, int64_t Rd, const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc,
+                              void* stream) {
+    if (I <= 0 || J <= 0 || I > INT32_MAX || J > INT32_MAX) return GSQ_ERR_SHAPE;
+    if (Rd <= 0 || Rd > INT32_MAX || (Rd % 64) != 0) return GSQ_ERR_SHAPE;
+    if (lda < Rd || ldb < Rd || ldc < J) return GSQ_ERR_SHAPE;
+    if ((lda % 8) != 0 || (ldb % 8) != 0 || (ldc % 8) != 0 || (J % 8) != 0) return GSQ_ERR_ALIGN;
+    if (!gemm_operand_fits(I, lda, Rd) || !gemm_operand_fits(J, ldb, Rd)) return GSQ_ERR_SHAPE;
+    GSQ_TRY(need(A));
+    GSQ_TRY(need(B));
+    GSQ_TRY(need(C));
+    return hip_status(gsq::launch_matmul_nt_bf16(I, J, Rd, A, lda, B, ldb, C, ldc,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_rmsnorm_bf16(int64_t rows, int64_t cols, const uint16_t* x, const float* gamma,
+                            float eps, uint16_t* y, void* stream) {
+    if (rows <= 0 || rows > INT32_MAX || cols <= 0 || cols > kMaxCoords / rows) return GSQ_ERR_SHAPE;
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return GSQ_ERR_PARAM;
+    GSQ_TRY(need(x));
+    GSQ_TRY(need(gamma));
+    GSQ_TRY(need(y));
+    return hip_status(gsq::launch_rmsnorm(rows, cols, x, gamma, eps, y,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_softmax_causal_bf16(int64_t n, const uint16_t* S, float scale, uint16_t* P,
+                                   void* stream) {
+    if (n <= 0 || n > INT32_MAX || n > kMaxCoords / n) return GSQ_ERR_SHAPE;
+    if (!std::isfinite(scale)) return GSQ_ERR_PARAM;
+    GSQ_TRY(need(S));
+    GSQ_TRY(need(P));
+    return hip_status(gsq::launch_softmax_causal(n, S, scale, P, static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_silu_mul_bf16(int64_t n, const uint16_t* gate, const uint16_t* up, uint16_t* act,
+                             void* stream) {
+    if (n < 0 || n > kMaxCoords) return GSQ_ERR_SHAPE;
+    if (n == 0) return GSQ_OK;
+    GSQ_TRY(need(gate));
+    GSQ_TRY(need(up));
+    GSQ_TRY(need(act));
+    return hip_status(gsq::launch_silu_mul(n, gate, up, act, static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_add_bf16(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
+                        void* stream) {
+    if (n < 0 || n > kMaxCoords) return GSQ_ERR_SHAPE;
+    if (n == 0) return GSQ_OK;
+    GSQ_TRY(need(a));
+    GSQ_TRY(need(b));
+    GSQ_TRY(need(out));
+    return hip_status(gsq::launch_add(n, a, b, out, static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_dequant_bf16(const gsq_layer* layer, const uint8_t* codes,
+                            const uint16_t* scales_f16, uint16_t* W, void* stream) {
+    LayerDesc d;
+    GSQ_TRY(check_layer(layer, &d));
+    GSQ_TRY(need(codes));
+    GSQ_TRY(need(scales_f16));
+    GSQ_TRY(need(W));
+    return hip_status(gsq::launch_dequant(d, codes, scales_f16, W, static_cast<hipStream_t>(stream)));
+}
+
 gsq_status gsq_relax_fwd(const gsq_layer* layer, const float* logits, const float* scales,
                          const uint8_t* init_codes, const void* W, uint32_t step, float tau,
                          float noise_scale, uint16_t* dW_bf16, float* w_soft_dbg, void* stream) {

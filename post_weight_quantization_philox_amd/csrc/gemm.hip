@@ -581,6 +581,13 @@ hipError_t launch_gram(int64_t tokens, int64_t cols, const uint16_t* XT, uint16_
                               static_cast<int>(tokens), H, cols, 1.0f, nullptr, st);
 }
 
+hipError_t launch_matmul_nt_bf16(int64_t I, int64_t J, int64_t Rd, const uint16_t* A, int64_t lda,
+                                 const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc,
+                                 hipStream_t st) {
+    return run_gemm<EPI_BF16>(A, lda, B, ldb, static_cast<int>(I), static_cast<int>(J),
+                              static_cast<int>(Rd), C, ldc, 1.0f, nullptr, st);
+}
+
 hipError_t launch_gram_f32(int64_t tokens, int64_t cols, const uint16_t* XT, float* H32,
                            hipStream_t st) {
     return run_gemm<EPI_F32_SCALED>(XT, tokens, XT, tokens, static_cast<int>(cols),

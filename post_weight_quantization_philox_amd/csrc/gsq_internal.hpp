@@ -74,6 +74,22 @@ hipError_t launch_gptq_factor(int64_t cols, float damp, const GptqWorkspace& ws,
 hipError_t launch_gptq_columns(const LayerDesc& d, const void* W, const GptqWorkspace& ws,
                                uint8_t* codes, float* logits, float init_logit, hipStream_t st);
 
+// Plain NT product C = A B^T in bf16 (fp32 accumulation), for the block forward.
+hipError_t launch_matmul_nt_bf16(int64_t I, int64_t J, int64_t Rd, const uint16_t* A, int64_t lda,
+                                 const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc,
+                                 hipStream_t st);
+// Block forward pieces (block.hip).
+hipError_t launch_rmsnorm(int64_t rows, int64_t cols, const uint16_t* x, const float* gamma,
+                          float eps, uint16_t* y, hipStream_t st);
+hipError_t launch_softmax_causal(int64_t n, const uint16_t* S, float scale, uint16_t* P,
+                                 hipStream_t st);
+hipError_t launch_silu_mul(int64_t n, const uint16_t* gate, const uint16_t* up, uint16_t* act,
+                           hipStream_t st);
+hipError_t launch_add(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
+                      hipStream_t st);
+hipError_t launch_dequant(const LayerDesc& d, const uint8_t* codes, const uint16_t* s16,
+                          uint16_t* W, hipStream_t st);
+
 hipError_t launch_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets, int64_t cols,
                                    const uint16_t* X, uint16_t* XT, hipStream_t st);
 
