@@ -5,6 +5,10 @@
 //   GEMM1  R^T = dW X^T      A = dW [M][K],   B = X   [N][K]  -> R^T [M][N] bf16,
 //                            plus the per-tile partial sum of R^2 (the loss);
 //   GEMM2  G   = 2 R^T X     A = R^T [M][N],  B = X^T [K][N]  -> G [M][K] fp32.
+// For a batch of experts each product is one grouped launch over all the
+// experts' tiles. The same kernel also forms the Gram matrix H = X^T X (bf16
+// or fp32 output), the Gram-form step G = 2 dW H with the loss sum dW * dW H
+// taken in its epilogue, and the plain bf16 products of the block forward.
 //
 // Tiling: 256x256 output tile per workgroup of 4 waves (2x2), each wave a
 // 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 blocks (256 fp32

@@ -42,9 +42,6 @@ hipError_t launch_noise_dump(const LayerDesc& d, uint32_t step, uint64_t first, 
                              uint32_t* out, hipStream_t st);
 
 // Reconstruction GEMMs.
-struct ExpertSpan {
-    int64_t tok0, ntok;  // token block of the expert (multiple of 64)
-};
 size_t recon_partials(int32_t n_experts, const int64_t* tok_offsets, int64_t rows_per_expert);
 hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t rows_per_expert,
                         int64_t cols, const uint16_t* X, const uint16_t* XT, const uint16_t* dW,
