@@ -344,6 +344,19 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     float lsum = 0.0f;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
+        // Gram form: this slab's dW values, loaded before the LDS round trip
+        // so that their latency overlaps it (zero outside the matrix).
+        uint2 dv[16];
+        if constexpr (EPI == EPI_F32_GRAM) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int c = lane + 64 * t;
+                const int grow = grow0 + a * 32 + (c >> 5), gcol = gcol0 + (c & 31) * 4;
+                dv[t] = (grow < g.I && gcol < g.J)
+                            ? *reinterpret_cast<const uint2*>(g.D + static_cast<int64_t>(grow) * g.ldd + gcol)
+                            : make_uint2(0u, 0u);
+            }
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
 #pragma unroll
@@ -388,8 +401,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
                 if (grow < g.I && gcol < g.J) {
                     const int64_t off = static_cast<int64_t>(grow) * g.ldc + gcol;
                     if constexpr (EPI == EPI_F32_GRAM) {
-                        const uint2 d = *reinterpret_cast<const uint2*>(
-                            g.D + static_cast<int64_t>(grow) * g.ldd + gcol);
+                        const uint2 d = dv[t];
                         lsum = __builtin_fmaf(bf16_lo(d.x), v.x, lsum);
                         lsum = __builtin_fmaf(bf16_hi(d.x), v.y, lsum);
                         lsum = __builtin_fmaf(bf16_lo(d.y), v.z, lsum);
