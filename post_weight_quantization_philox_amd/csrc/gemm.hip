@@ -342,20 +342,25 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     const int grow0 = i0 + wi * 128;
     const int gcol0 = j0 + wj * 128;
     float lsum = 0.0f;
+    // Gram form: the dW values a slab pairs with, loaded one slab ahead so
+    // their latency overlaps the previous slab's work (zero outside the
+    // matrix).
+    uint2 dv[2][16];
+    auto load_dv = [&](int a, uint2 (&d)[16]) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int c = lane + 64 * t;
+            const int grow = grow0 + a * 32 + (c >> 5), gcol = gcol0 + (c & 31) * 4;
+            d[t] = (grow < g.I && gcol < g.J)
+                       ? *reinterpret_cast<const uint2*>(g.D + static_cast<int64_t>(grow) * g.ldd + gcol)
+                       : make_uint2(0u, 0u);
+        }
+    };
+    if constexpr (EPI == EPI_F32_GRAM) load_dv(0, dv[0]);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-        // Gram form: this slab's dW values, loaded before the LDS round trip
-        // so that their latency overlaps it (zero outside the matrix).
-        uint2 dv[16];
         if constexpr (EPI == EPI_F32_GRAM) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int c = lane + 64 * t;
-                const int grow = grow0 + a * 32 + (c >> 5), gcol = gcol0 + (c & 31) * 4;
-                dv[t] = (grow < g.I && gcol < g.J)
-                            ? *reinterpret_cast<const uint2*>(g.D + static_cast<int64_t>(grow) * g.ldd + gcol)
-                            : make_uint2(0u, 0u);
-            }
+            if (a + 1 < 4) load_dv(a + 1, dv[(a + 1) & 1]);
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -401,7 +406,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
                 if (grow < g.I && gcol < g.J) {
                     const int64_t off = static_cast<int64_t>(grow) * g.ldc + gcol;
                     if constexpr (EPI == EPI_F32_GRAM) {
-                        const uint2 d = dv[t];
+                        const uint2 d = dv[a & 1][t];
                         lsum = __builtin_fmaf(bf16_lo(d.x), v.x, lsum);
                         lsum = __builtin_fmaf(bf16_hi(d.x), v.y, lsum);
                         lsum = __builtin_fmaf(bf16_lo(d.y), v.z, lsum);
