@@ -29,7 +29,7 @@
  *  - Layouts are row-major. Logits and their Lion momentum are planar
  *    [L][rows][cols] fp32 (plane k holds logit k of every coordinate), with
  *    L = 4 (2-bit), 2 (ternary: plane 0 mask, plane 1 sign), 5 (3-bit local
- *    shift: planes for offsets -2..+2). Scales and their momentum are
+ *    shift: planes for offsets -2..+2), 8 (full 3-bit grid). Scales and their momentum are
  *    [rows][cols/128] fp32. bf16 and fp16 tensors are passed as uint16_t bits.
  *  - All arguments are checked before anything is launched; a failed check
  *    returns its status and launches nothing. A HIP launch error returns
@@ -111,7 +111,7 @@ int gsq_abi_version(void);
 /* Static, NUL-terminated name of a status code. */
 const char* gsq_status_str(int status);
 
-/* Number of logits per coordinate of a grid (4, 2, 5), or 0 if unknown. */
+/* Number of logits per coordinate of a grid (4, 2, 5, 8), or 0 if unknown. */
 int gsq_num_logits(int grid);
 
 /* Warm start by round-to-nearest (the pages start from GPTQ or a GGUF
@@ -202,7 +202,8 @@ gsq_status gsq_dequant_bf16(const gsq_layer* layer, const uint8_t* codes,
 
 /* Relaxed forward (agihunt.info method paragraph: soft weighted sum of grid
  * points). With noise n_k drawn for `step` and eta = noise_scale:
- *   2-bit / local shift: p = softmax((l + eta*g)/tau), g standard Gumbel,
+ *   2-bit / 3-bit (local shift or full grid): p = softmax((l + eta*g)/tau),
+ *                        g standard Gumbel,
  *                        w_hat = sum_k p_k v_k;
  *   ternary: a = sigmoid((l_m + eta*n_m)/tau), b = sigmoid((l_s + eta*n_s)/tau),
  *            n standard logistic, w_hat = a * (2b - 1);
@@ -293,7 +294,7 @@ gsq_status gsq_recon_gram(int64_t rows, int64_t cols, const uint16_t* H,
 /* Relaxed backward and Lion, in place (agihunt.info method and optimizer
  * paragraphs). Regenerates the step's noise (same `step`, `tau` and
  * `noise_scale` as the forward) and, with G = dLoss/dW_soft:
- *   2-bit / local shift: dL/dl_k = G * s * p_k * (v_k - w_hat) / tau;
+ *   2-bit / 3-bit: dL/dl_k = G * s * p_k * (v_k - w_hat) / tau;
  *   ternary: dL/dl_m = G * s * a(1-a)(2b-1) / tau, dL/dl_s = G * s * 2a b(1-b) / tau;
  *   dL/ds_g = sum over the 128 coordinates of the group of G * w_hat;
  * then one Lion update of every logit and every scale with its momentum,
@@ -330,10 +331,12 @@ gsq_status gsq_relax_bwd_lion_fwd(const gsq_layer* layer, const float* G, float*
 /* Collapse to hard codes after annealing (agihunt.info method paragraph) in
  * the symmetric group-128 format with 16-bit scales (takeaway paragraph;
  * the 2.13 / 3.13 / 1.71 bits per parameter of the results table).
- *   codes: 2-bit argmax_k l_k (first index on ties); local shift
- *   clamp(c0 + argmax - 2, 0, 7); ternary t + 1, t = [l_m >= 0]*(l_s >= 0 ? 1 : -1).
+ *   codes: 2-bit and full 3-bit argmax_k l_k (first index on ties); local
+ *   shift clamp(c0 + argmax - 2, 0, 7); ternary t + 1,
+ *   t = [l_m >= 0]*(l_s >= 0 ? 1 : -1).
  *   codes       optional out [rows][cols] uint8
- *   packed      optional out [rows][cols*b/32] uint32, b = 2, 2, 3 bits; per
+ *   packed      optional out [rows][cols*b/32] uint32, b = 2 (2-bit,
+ *               ternary) or 3 (3-bit); per
  *               row a little-endian LSB-first bit-stream, code j in bits
  *               [b*j, b*j + b)
  *   scales_f16  optional out [rows][cols/128] fp16 bits (nearest even) */
