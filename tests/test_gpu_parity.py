@@ -216,10 +216,16 @@ def test_relax_bwd_lion(dev, grid, tau, shape):
 # Reconstruction GEMMs
 # ----------------------------------------------------------------------------
 
+# 67 experts of 32 rows with 0, 64 or 128 tokens each: more experts than one
+# grouped launch takes (64), so each product runs as two launches.
+_OFFS67 = [0] + np.cumsum(np.random.default_rng(67).choice([0, 64, 128], 67)).tolist()
+
+
 @pytest.mark.parametrize("M,N,K,offs", [
     (512, 256, 512, None),            # one linear layer, several tiles
     (300, 192, 384, None),            # ragged rows, partial tiles
     (3 * 256, 320, 256, [0, 128, 128, 320]),   # three experts, one with no tokens
+    (67 * 32, _OFFS67[-1], 256, _OFFS67),      # two grouped launches per product
 ])
 def test_recon_loss_grad(dev, M, N, K, offs):
     import torch
