@@ -74,6 +74,28 @@ def measured_traffic(workload: str, kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
+def host_info() -> dict:
+    """The host the oracle ran on: CPU model, logical CPUs, the affinity mask's
+    size and the thread-count environment variables."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    env = {k: os.environ[k] for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                      "MKL_NUM_THREADS") if k in os.environ}
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "affinity": affinity,
+            "thread_env": env}
+
+
 def cpu_baseline(data, rows: int):
     """The oracle (NumPy fp64) on the first ``rows`` rows of a dense layer:
     one full step (relaxed forward, both products against all tokens,
@@ -95,7 +117,7 @@ def cpu_baseline(data, rows: int):
     oracle.step(state, W, X, wl.grid, 0, 1.0, 0, 0, 1e-3, 1e-5, bf16_dW=True)
     dt = time.perf_counter() - t0
     return {"value": rows * W.shape[1] / dt, "unit": "weights/s", "cores": blas_threads,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_info(),
             "sample": f"one full step on rows 0..{rows - 1} of the {wl.rows}x{wl.cols} layer "
                       f"({rows * W.shape[1]} weights) against all {X.shape[0]} tokens, {dt:.1f} s; "
                       f"NumPy elementwise work on one thread, BLAS on {blas_threads}"}
