@@ -24,8 +24,8 @@ import numpy as np
 import torch
 
 from . import (GRID_INT3_LOCAL, DTYPE_BF16, DTYPE_F32, N_LOGITS, CODE_BITS, GsqLayer,
-               GsqLion, gsq_init_rtn, gsq_gptq_workspace_bytes, gsq_init_gptq, gsq_relax_fwd, gsq_recon_workspace_bytes,
-               gsq_recon_loss_grad, gsq_transpose_tokens, gsq_gram,
+               GsqLion, gsq_init_rtn, gsq_gptq_workspace_bytes, gsq_init_gptq, gsq_relax_fwd,
+               gsq_recon_workspace_bytes, gsq_recon_loss_grad, gsq_transpose_tokens, gsq_gram,
                gsq_recon_gram_workspace_bytes, gsq_recon_gram, gsq_relax_bwd_lion,
                gsq_relax_bwd_lion_fwd, gsq_harden_pack)
 
