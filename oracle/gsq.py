@@ -550,9 +550,11 @@ def step(state: dict, W, X, grid: int, t: int, tau: float, seed: int,
          stream: int, lr_logit: float, lr_scale: float, beta1: float = 0.9,
          beta2: float = 0.99, weight_decay: float = 0.0,
          noise_scale: float = 1.0, bf16_dW: bool = False, group: int = 128,
-         bf16_RT: bool = False, H=None):
+         bf16_RT: bool = False, H=None, row0: int = 0):
     """One full relaxed-quantization step on a whole layer, in place on
     ``state`` (``logits``, ``mom``, ``scales``, ``scale_mom``, ``codes``).
+    ``row0`` places the rows given at that row of a larger layer (it only
+    moves the noise counters; rows are independent in the objective).
 
     Forward relaxation, reconstruction loss and gradient, backward to the
     logits and scales, Lion on both. ``bf16_dW`` rounds dW to bfloat16 before
@@ -563,7 +565,7 @@ def step(state: dict, W, X, grid: int, t: int, tau: float, seed: int,
     """
     codes = state["codes"] if grid == GRID_INT3_LOCAL else None
     f = relax_fwd(state["logits"], state["scales"], W, grid, seed, stream, t,
-                  tau, noise_scale, codes, 0, group)
+                  tau, noise_scale, codes, row0, group)
     dW = round_bf16(f["dW"]).astype(np.float64) if bf16_dW else f["dW"]
     if H is not None:
         loss, G = recon_loss_grad_gram(dW, H)
@@ -572,7 +574,7 @@ def step(state: dict, W, X, grid: int, t: int, tau: float, seed: int,
         if bf16_RT:
             G = 2.0 * (round_bf16(RT).astype(np.float64) @ np.asarray(X, dtype=np.float64))
     gl, gs = relax_bwd(G, state["logits"], state["scales"], grid, seed, stream,
-                       t, tau, noise_scale, codes, 0, group)
+                       t, tau, noise_scale, codes, row0, group)
     state["logits"], state["mom"] = lion(state["logits"], gl, state["mom"],
                                          lr_logit, beta1, beta2, weight_decay)
     state["scales"], state["scale_mom"] = lion(state["scales"], gs,

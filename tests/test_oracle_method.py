@@ -557,3 +557,31 @@ def test_row_chunks_agree_with_whole_layer(grid):
     np.testing.assert_array_equal(part, full[r])
     np.testing.assert_array_equal(pgl, gl[:, r])
     np.testing.assert_array_equal(pgs, gs[r])
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+def test_step_on_row_blocks_equals_whole_layer_step(grid):
+    # Rows are independent in the objective (R[:, r] = X dW[r]^T and G[r] =
+    # 2 R[:, r]^T X), so whole steps on row blocks placed with row0 give the
+    # rows of the whole-layer step, and their losses sum to its loss.
+    M, K, N = 5, 256, 64
+    W = layer(M, K)
+    X = np.random.default_rng(3).normal(size=(N, K))
+    s, c0, lg = oracle.init_rtn(W, grid)
+
+    def fresh(r):
+        return {"logits": lg[:, r].copy(), "mom": np.zeros_like(lg[:, r]), "scales": s[r].copy(),
+                "scale_mom": np.zeros_like(s[r]), "codes": c0[r].copy()}
+
+    whole = fresh(slice(0, M))
+    blocks = [(slice(0, 2), fresh(slice(0, 2))), (slice(2, M), fresh(slice(2, M)))]
+    for t, tau in enumerate((1.0, 0.5, 0.2)):
+        loss = oracle.step(whole, W, X, grid, t, tau, 7, 1, 5e-2, 1e-4, bf16_dW=True, bf16_RT=True)
+        parts = [oracle.step(st, W[r], X, grid, t, tau, 7, 1, 5e-2, 1e-4, bf16_dW=True,
+                             bf16_RT=True, row0=r.start) for r, st in blocks]
+        assert abs(sum(parts) - loss) <= 1e-12 * loss
+    for r, st in blocks:
+        for key in ("logits", "mom"):
+            np.testing.assert_array_equal(st[key], whole[key][:, r])
+        for key in ("scales", "scale_mom"):
+            np.testing.assert_array_equal(st[key], whole[key][r])
