@@ -180,3 +180,58 @@ def test_trajectory_from_gptq_start():
            hard_after=oracle.hard_loss(c_ref, state["scales"], d["W"], d["X"], grid))
     assert rel.max() <= 2e-3
     assert agree >= 0.999
+
+
+def test_expert_batch_trajectory_matches_oracle():
+    """An annealed solve of an expert batch (grouped products; one expert
+    without tokens, one whose tokens the solver pads to 64) against the
+    oracle's step loop run expert by expert, each expert's rows placed at
+    their rows in the batch for the noise counters. The batch loss is the sum
+    of the experts' losses."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver, tau_schedule
+    dev = device()
+    grid = oracle.GRID_INT2
+    E, rpe, K, T, sid = 5, 128, 256, 24, 9
+    counts = [0, 64, 128, 192, 40]
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    rng = np.random.default_rng(11)
+    W_bits = synthetic.bf16_bits(rng.normal(0, 0.02, (E * rpe, K)).astype(np.float32))
+    X_bits = synthetic.bf16_bits(rng.normal(0, 1, (int(offs[-1]), K)).astype(np.float32))
+    W = synthetic.bf16_to_f32(W_bits)
+    X = synthetic.bf16_to_f32(X_bits).astype(np.float64)
+    lr_logit, lr_scale = 1e-1, 1e-5
+    taus = tau_schedule(T, 1.0, 0.1)
+    solver = LayerSolver(to_dev_bf16(W_bits, dev), to_dev_bf16(X_bits, dev), grid, tok_offsets=offs,
+                         rows_per_expert=rpe, seed=0, stream_id=sid,
+                         lion=g.GsqLion.make(lr_logit=lr_logit, lr_scale=lr_scale))
+    solver.relax_fwd(0, taus[0])
+    gpu_losses = []
+    for t in range(T):
+        solver.step_fused(t, taus[t], taus[t + 1] if t + 1 < T else None)
+        gpu_losses.append(float(solver.loss.item()))
+    codes = solver.harden()[0].cpu().numpy()
+
+    s, c0, lg = oracle.init_rtn(W, grid)
+    ref = np.zeros(T)
+    c_ref = np.zeros_like(codes)
+    for e in range(E):
+        r = slice(e * rpe, (e + 1) * rpe)
+        st = {"logits": lg[:, r].copy(), "mom": np.zeros_like(lg[:, r]), "scales": s[r].copy(),
+              "scale_mom": np.zeros_like(s[r]), "codes": c0[r]}
+        Xe = X[offs[e]:offs[e + 1]]
+        for t in range(T):
+            ref[t] += oracle.step(st, W[r], Xe, grid, t, taus[t], 0, sid, lr_logit, lr_scale,
+                                  bf16_dW=True, bf16_RT=True, row0=e * rpe)
+        c_ref[r] = oracle.harden(st["logits"], grid, c0[r])
+    rel = np.abs(np.array(gpu_losses) - ref) / ref
+    agree = float(np.mean(codes == c_ref))
+    moved = float(np.mean(c_ref != c0))
+    idle = float(np.mean(c_ref[:rpe] != c0[:rpe]))
+    report("expert batch trajectory", max_rel_loss=float(rel.max()), code_agreement=agree,
+           codes_moved_from_init=moved, moved_without_tokens=idle)
+    assert rel.max() <= 2e-3
+    assert agree >= 0.999
+    assert moved > 0.001
+    assert idle == 0.0                # no tokens: zero gradient, Lion leaves the logits alone
