@@ -306,7 +306,8 @@ def test_beyond_32bit_offsets():
 # within the steps: a ternary code changes only when a logit crosses 0, so
 # the ternary layer starts nearer to it.
 @pytest.mark.parametrize("name,init_logit,lr_logit", [("qproj4096_int2", 2.0, 5e-2),
-                                                      ("downproj4096x14336_ternary", 0.5, 5e-2)])
+                                                      ("downproj4096x14336_ternary", 0.5, 5e-2),
+                                                      ("gateproj28672x8192_int3local", 2.0, 5e-2)])
 def test_fullsize_trajectory_sampled_rows(name, init_logit, lr_logit):
     """An annealed solve of the whole layer in the launch configuration the
     bench times (objective, then fused backward + Lion + next forward)
