@@ -4,12 +4,12 @@
 // N consecutive coordinates i0..i0+N-1 of the flattened layer (i0 = N * global
 // thread id), so every planar logit / momentum plane is read and written as
 // one N*4-byte vector per thread. 128/N threads cover one scale group of 128
-// coordinates and reduce it with lane shuffles. N is 2 for the 2-bit and full
-// 3-bit grids (halving the registers a thread holds, so that more waves are
-// in flight to hide HBM latency) and 4 for ternary (already at full
-// occupancy) and local shift (whose 5 logits need N = 4 for the N
-// coordinates' noise to be a whole number of Philox blocks, L*N/4, so that no
-// word is generated twice).
+// coordinates and reduce it with lane shuffles. N is 2 for the 2-bit, full
+// 3-bit and ternary grids: 8-byte vectors per plane stream faster than
+// 16-byte ones on this access mix, and the 2-bit kernels hold half the
+// registers, so more waves are in flight. Local shift keeps N = 4: its 5
+// logits need it for the N coordinates' noise to be a whole number of Philox
+// blocks, L*N/4, so that no word is generated twice.
 #include <type_traits>
 
 #include "gsq_internal.hpp"
@@ -24,7 +24,7 @@ template <int GRID> struct GridT;
 // L logits per coordinate, q_max, code bits, and N coordinates per thread in
 // the relax kernels.
 template <> struct GridT<GSQ_GRID_INT2> { static constexpr int L = 4; static constexpr int QMAX = 3; static constexpr int BITS = 2; static constexpr int N = 2; };
-template <> struct GridT<GSQ_GRID_TERNARY> { static constexpr int L = 2; static constexpr int QMAX = 1; static constexpr int BITS = 2; static constexpr int N = 4; };
+template <> struct GridT<GSQ_GRID_TERNARY> { static constexpr int L = 2; static constexpr int QMAX = 1; static constexpr int BITS = 2; static constexpr int N = 2; };
 template <> struct GridT<GSQ_GRID_INT3_LOCAL> { static constexpr int L = 5; static constexpr int QMAX = 7; static constexpr int BITS = 3; static constexpr int N = 4; };
 template <> struct GridT<GSQ_GRID_INT3> { static constexpr int L = 8; static constexpr int QMAX = 7; static constexpr int BITS = 3; static constexpr int N = 2; };
 
