@@ -1,6 +1,8 @@
 // Device helpers shared by the GSQ kernels (gfx950, wave64).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,6 +88,49 @@ struct NoiseStream {
         }
     }
 };
+
+// The same noise when N*L is 2 mod 4 (i0 a multiple of N, so i0*L is even):
+// the thread's N*L words start at word 0 or 2 of block i0*L/4 ("shifted").
+// Blocks are generated on demand as in NoiseStream, at most two live; both
+// placements of coordinate C's words lie in the same two blocks, and each
+// word is selected from its block for the thread's placement.
+template <int L, int N>
+struct NoiseStreamU {
+    static_assert((L * N) % 4 == 2, "for N*L = 2 mod 4");
+    uint64_t b0;
+    bool shifted;
+    uint32_t step, sid;
+    Key key;
+    uint32_t cur[4], nxt[4];
+
+    __device__ __forceinline__ NoiseStreamU(uint64_t i0, uint32_t step_, uint32_t sid_, Key key_)
+        : b0((i0 * L) >> 2), shifted(((i0 * L) & 3u) != 0), step(step_), sid(sid_), key(key_) {}
+
+    template <int C>
+    __device__ __forceinline__ void words(uint32_t (&w)[L]) {
+        constexpr int first = C * L;
+        constexpr int hi = (first + L - 1 + 2) / 4;            // last block (shifted)
+        constexpr int done = C == 0 ? -1 : (first - 1 + 2) / 4;  // last block generated before
+        static_assert(first / 4 >= hi - 1, "a coordinate's words span at most two blocks");
+#pragma unroll
+        for (int b = done + 1; b <= hi; ++b) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+            philox_block(b0 + b, step, sid, key, nxt);
+        }
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            const int u = first + j, v = u + 2;
+            const uint32_t a = (u / 4 == hi) ? nxt[u & 3] : cur[u & 3];
+            const uint32_t c = (v / 4 == hi) ? nxt[v & 3] : cur[v & 3];
+            w[j] = shifted ? c : a;
+        }
+    }
+};
+
+template <int L, int N>
+using NoiseFor = typename std::conditional<(L * N) % 4 == 0, NoiseStream<L, N>,
+                                           NoiseStreamU<L, N>>::type;
 
 // Uniform in (0,1): top 24 bits forced odd, times 2^-24 (exact in fp32).
 __device__ __forceinline__ float uniform24(uint32_t x) {

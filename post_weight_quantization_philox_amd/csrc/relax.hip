@@ -4,12 +4,12 @@
 // N consecutive coordinates i0..i0+N-1 of the flattened layer (i0 = N * global
 // thread id), so every planar logit / momentum plane is read and written as
 // one N*4-byte vector per thread. 128/N threads cover one scale group of 128
-// coordinates and reduce it with lane shuffles. N is 2 for the 2-bit, full
-// 3-bit and ternary grids: 8-byte vectors per plane stream faster than
-// 16-byte ones on this access mix, and the 2-bit kernels hold half the
-// registers, so more waves are in flight. Local shift keeps N = 4: its 5
-// logits need it for the N coordinates' noise to be a whole number of Philox
-// blocks, L*N/4, so that no word is generated twice.
+// coordinates and reduce it with lane shuffles. N is 2 for every grid:
+// 8-byte vectors per plane stream faster than 16-byte ones on this access
+// mix, and a thread holds half the registers, so more waves are in flight.
+// With 5 logits (local shift) two coordinates are 10 noise words, which start
+// at word 0 or 2 of a Philox block (NoiseStreamU); the other grids' words are
+// whole blocks (NoiseStream).
 #include <type_traits>
 
 #include "gsq_internal.hpp"
@@ -25,7 +25,7 @@ template <int GRID> struct GridT;
 // the relax kernels.
 template <> struct GridT<GSQ_GRID_INT2> { static constexpr int L = 4; static constexpr int QMAX = 3; static constexpr int BITS = 2; static constexpr int N = 2; };
 template <> struct GridT<GSQ_GRID_TERNARY> { static constexpr int L = 2; static constexpr int QMAX = 1; static constexpr int BITS = 2; static constexpr int N = 2; };
-template <> struct GridT<GSQ_GRID_INT3_LOCAL> { static constexpr int L = 5; static constexpr int QMAX = 7; static constexpr int BITS = 3; static constexpr int N = 4; };
+template <> struct GridT<GSQ_GRID_INT3_LOCAL> { static constexpr int L = 5; static constexpr int QMAX = 7; static constexpr int BITS = 3; static constexpr int N = 2; };
 template <> struct GridT<GSQ_GRID_INT3> { static constexpr int L = 8; static constexpr int QMAX = 7; static constexpr int BITS = 3; static constexpr int N = 2; };
 
 // Element i of a tensor whose planes start at wave-uniform bases. With O32
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void relax_fwd_kernel(
     const float s = scales[i0 >> 7];
     uint32_t cw = 0;
     if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = load_codes<N>(codes, ix);
-    NoiseStream<L, N> ns(i0, step, sid, key);
+    NoiseFor<L, N> ns(i0, step, sid, key);
     float out[N];
     forN<N>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
     if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = load_codes<N>(codes, ix);
     float gsum = 0.0f;
     {
-        NoiseStream<L, N> ns(i0, step, sid, key);
+        NoiseFor<L, N> ns(i0, step, sid, key);
         const float gs_tau = s * tk.invtau;
         // Each coordinate's gradient goes straight into its Lion update, so
         // no gradient array stays live (fewer registers, more waves in flight).
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
         // W is only needed here; its load overlaps the next-step noise.
         float w[N];
         load_w<N>(W, WBF16, ix, w);
-        NoiseStream<L, N> ns(i0, next_step, sid, key);
+        NoiseFor<L, N> ns(i0, next_step, sid, key);
         float out[N];
         forN<N>([&](auto cc) {
             constexpr int c = decltype(cc)::value;
