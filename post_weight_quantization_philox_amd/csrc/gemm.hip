@@ -39,6 +39,7 @@ constexpr uint32_t kOob = 0x7FFFFF00u;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Epilogues: bf16 output plus the tile's sum of squares (GEMM1); fp32 output
 // times alpha (GEMM2); plain bf16 output (the Gram matrix); fp32 output times
@@ -412,8 +413,11 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
                         lsum = __builtin_fmaf(bf16_lo(d.y), v.z, lsum);
                         lsum = __builtin_fmaf(bf16_hi(d.y), v.w, lsum);
                     }
-                    *reinterpret_cast<float4*>(static_cast<float*>(g.C) + off) =
-                        make_float4(g.alpha * v.x, g.alpha * v.y, g.alpha * v.z, g.alpha * v.w);
+                    // G is read once, by the next kernel: a nontemporal
+                    // store (the 64-expert recon 2.45 -> 2.26 ms).
+                    __builtin_nontemporal_store(
+                        f32x4{g.alpha * v.x, g.alpha * v.y, g.alpha * v.z, g.alpha * v.w},
+                        reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off));
                 }
             }
         }
