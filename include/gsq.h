@@ -134,9 +134,9 @@ gsq_status gsq_init_rtn(const gsq_layer* layer, const void* W, float* scales,
                         void* stream);
 
 /* Workspace bytes of gsq_init_gptq for a layer of rows x cols: the fp32 Gram
- * matrix, one fp64 cols x cols factor, fp64 rounding errors of the whole
- * layer and one 128-column block of feedback (about 12*cols^2 + 8*rows*cols
- * bytes). 0 for invalid sizes. */
+ * matrix, one fp64 cols x cols factor, the fp64 error feedback of the whole
+ * layer and one 128-column block of rounding errors (about 12*cols^2 +
+ * 8*rows*cols bytes). 0 for invalid sizes. */
 size_t gsq_gptq_workspace_bytes(int64_t rows, int64_t cols);
 
 /* GPTQ warm start (Frantar et al. 2022), the initialisation the pages start

@@ -16,14 +16,16 @@
 //
 // Steps: H = X^T X (fp32, matrix cores, gemm.hip); lambda = damp * mean
 // diag(H) (a zero diagonal entry counts as 1); A = J (H + lambda I) J in fp64
-// (lower triangle); blocked right-looking Cholesky of A in place (32-column
-// panels: the diagonal block in LDS, a triangular solve for the rows below,
-// a symmetric rank-32 update of the trailing lower triangle); then
+// (lower triangle); blocked right-looking Cholesky of A in place (64-column
+// panels: the diagonal block in LDS by one wave, a triangular solve for the
+// rows below, a symmetric rank-64 update of the trailing lower triangle); then
 // V_ij = R_ij / R_jj for i < j, written into the unused upper triangle of A;
-// then for every 128-column group: P = D[:, <j0] V[<j0, group] (fp64 tiled
-// product of the earlier columns' errors D = W - Q), and one thread per row
-// runs the 128 columns of the group sequentially with the group's block of V
-// and the row's errors in LDS. Group scales are the absmax scales of the
+// then for every 128-column group: one thread per row runs the group's 128
+// columns sequentially (the group's block of V and the row's errors in LDS),
+// from targets that already hold the feedback of every earlier group; then
+// the group's errors D = W - Q are fed forward into all later columns at once
+// (P[:, later] += D V[group, later], an fp64 tiled product over the group's
+// 128 columns that covers the whole GPU). Group scales are the absmax scales of the
 // original weights (GPTQ's static groups), i.e. the round-to-nearest scales.
 #include <math.h>
 
@@ -33,7 +35,7 @@ namespace gsq {
 
 namespace {
 
-constexpr int kPanel = 32;     // Cholesky panel width
+constexpr int kPanel = 64;     // Cholesky panel width
 constexpr int kBlock = 128;    // GPTQ column block = scale group
 
 template <int GRID> struct GT;
@@ -76,40 +78,37 @@ __global__ __launch_bounds__(256) void reverse_damp_kernel(const float* __restri
     A[i * K + j] = v;
 }
 
-// Cholesky of the kPanel x kPanel diagonal block at (p, p), in LDS. A pivot
-// that is not positive records its 1-based column in *info (first failure
-// only) and is replaced by 1 so the rest stays finite.
-__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ A, int64_t K, int64_t p,
-                                                         int32_t* __restrict__ info) {
+// Cholesky of the kPanel x kPanel diagonal block at (p, p), in LDS, by one
+// wave (kPanel = 64 lanes, lane i owns row i), column by column: column k is
+// its entries minus the products with the finished columns, then scaled by
+// the pivot's square root. A pivot that is not positive records its 1-based
+// column in *info (first failure only) and is replaced by 1 so the rest
+// stays finite.
+__global__ __launch_bounds__(kPanel) void potrf_diag_kernel(double* __restrict__ A, int64_t K,
+                                                            int64_t p, int32_t* __restrict__ info) {
+    static_assert(kPanel == 64, "one lane per row of the diagonal block");
     __shared__ double t[kPanel][kPanel + 1];
-    const int tid = threadIdx.x;
-    for (int e = tid; e < kPanel * kPanel; e += 256) {
-        const int i = e / kPanel, j = e % kPanel;
-        t[i][j] = (j <= i) ? A[(p + i) * K + p + j] : 0.0;
-    }
+    const int i = threadIdx.x;
+    for (int j = 0; j < kPanel; ++j) t[i][j] = (j <= i) ? A[(p + i) * K + p + j] : 0.0;
     __syncthreads();
     for (int k = 0; k < kPanel; ++k) {
-        if (tid == 0) {
-            double d = t[k][k];
-            if (!(d > 0.0)) {
+        double v = 0.0;
+        if (i >= k) {
+            v = t[i][k];
+            for (int m = 0; m < k; ++m) v = fma(-t[i][m], t[k][m], v);
+        }
+        if (i == k) {
+            if (!(v > 0.0)) {
                 if (*info == 0) *info = static_cast<int32_t>(p + k + 1);
-                d = 1.0;
+                v = 1.0;
             }
-            t[k][k] = sqrt(d);
+            t[k][k] = sqrt(v);
         }
         __syncthreads();
-        if (tid > k && tid < kPanel) t[tid][k] /= t[k][k];
-        __syncthreads();
-        for (int e = tid; e < kPanel * kPanel; e += 256) {
-            const int i = e / kPanel, j = e % kPanel;
-            if (j > k && i >= j) t[i][j] -= t[i][k] * t[j][k];
-        }
+        if (i > k) t[i][k] = v / t[k][k];
         __syncthreads();
     }
-    for (int e = tid; e < kPanel * kPanel; e += 256) {
-        const int i = e / kPanel, j = e % kPanel;
-        if (j <= i) A[(p + i) * K + p + j] = t[i][j];
-    }
+    for (int j = 0; j <= i; ++j) A[(p + i) * K + p + j] = t[i][j];
 }
 
 // Rows below the panel: x L11^T = a, one thread per row.
@@ -136,43 +135,63 @@ __global__ __launch_bounds__(256) void trsm_kernel(double* __restrict__ A, int64
     for (int k = 0; k < kPanel; ++k) A[i * K + p + k] = x[k];
 }
 
-// Trailing update A22 -= L21 L21^T on the lower triangle, 64x64 tiles
-// enumerated over the lower triangle of tiles; 4x4 outputs per thread.
+// Trailing update A22 -= L21 L21^T on the lower triangle: 128x128 tiles
+// enumerated over the lower triangle of tiles, 8x8 outputs per thread (two
+// fp64 FMAs per LDS value read), the panel's kPanel columns in chunks of 16
+// staged through LDS (transposed: k-major).
+constexpr int kSyrk = 128;
 __global__ __launch_bounds__(256) void syrk_kernel(double* __restrict__ A, int64_t K, int64_t p) {
-    __shared__ double Pi[64][kPanel + 1];
-    __shared__ double Pj[64][kPanel + 1];
+    __shared__ double Pi[16][kSyrk + 2];
+    __shared__ double Pj[16][kSyrk + 2];
     const int64_t q = p + kPanel;
     const int64_t x = blockIdx.x;
     int64_t bi = static_cast<int64_t>((sqrt(8.0 * static_cast<double>(x) + 1.0) - 1.0) * 0.5);
     while (bi * (bi + 1) / 2 > x) --bi;
     while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
     const int64_t bj = x - bi * (bi + 1) / 2;
-    const int64_t r0 = q + bi * 64, c0 = q + bj * 64;
-    for (int e = threadIdx.x; e < 64 * kPanel; e += 256) {
-        const int r = e / kPanel, k = e % kPanel;
-        Pi[r][k] = (r0 + r < K) ? A[(r0 + r) * K + p + k] : 0.0;
-        Pj[r][k] = (c0 + r < K) ? A[(c0 + r) * K + p + k] : 0.0;
-    }
-    __syncthreads();
+    const int64_t r0 = q + bi * kSyrk, c0 = q + bj * kSyrk;
     const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
-    double acc[4][4] = {};
+    // The tile's current values are loaded first, so their latency overlaps
+    // the panel products that are subtracted from them.
+    double acc[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int64_t row = r0 + ty + 16 * u;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const int64_t col = c0 + tx + 16 * v;
+            acc[u][v] = (row < K && col <= row) ? A[row * K + col] : 0.0;
+        }
+    }
+    for (int k0 = 0; k0 < kPanel; k0 += 16) {
+        for (int e = threadIdx.x; e < 16 * kSyrk; e += 256) {
+            const int r = e >> 4, k = e & 15;
+            Pi[k][r] = (r0 + r < K) ? A[(r0 + r) * K + p + k0 + k] : 0.0;
+            Pj[k][r] = (c0 + r < K) ? A[(c0 + r) * K + p + k0 + k] : 0.0;
+        }
+        __syncthreads();
 #pragma unroll 4
-    for (int k = 0; k < kPanel; ++k) {
-        double a[4], b[4];
+        for (int k = 0; k < 16; ++k) {
+            double a[8], b[8];
+            // rows ty + 16u, columns tx + 16v: consecutive lanes hold
+            // consecutive columns, which are contiguous in A
 #pragma unroll
-        for (int u = 0; u < 4; ++u) { a[u] = Pi[ty * 4 + u][k]; b[u] = Pj[tx * 4 + u][k]; }
+            for (int u = 0; u < 8; ++u) { a[u] = -Pi[k][ty + 16 * u]; b[u] = Pj[k][tx + 16 * u]; }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 8; ++u)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+                for (int v = 0; v < 8; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+        }
+        __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t row = r0 + ty * 4 + u;
+    for (int u = 0; u < 8; ++u) {
+        const int64_t row = r0 + ty + 16 * u;
+        if (row >= K) continue;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t col = c0 + tx * 4 + v;
-            if (row < K && col <= row) A[row * K + col] -= acc[u][v];
+        for (int v = 0; v < 8; ++v) {
+            const int64_t col = c0 + tx + 16 * v;
+            if (col <= row) A[row * K + col] = acc[u][v];
         }
     }
 }
@@ -187,43 +206,64 @@ __global__ __launch_bounds__(256) void make_v_kernel(double* __restrict__ A, int
     A[i * K + j] = A[ri * K + rj] / A[rj * K + rj];
 }
 
-// P[c][r] = sum_{i < j0} Dt[i][r] V[i][j0 + c] for c < kBlock, r < M (both
-// column-major over r). 64x64 output tiles, 4x4 per thread, contraction in
-// chunks of 16 staged through LDS.
-__global__ __launch_bounds__(256) void gptq_gemm_kernel(const double* __restrict__ Dt,
-                                                        const double* __restrict__ A, int64_t K,
-                                                        int64_t M, int64_t j0, double* __restrict__ P) {
-    __shared__ double sD[16][64 + 1];
-    __shared__ double sV[16][64 + 1];
-    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
-    const int c0 = blockIdx.y * 64;
+// Feed group [j0, j0 + kBlock)'s errors into every later column:
+// P[c][r] (+)= sum_{k < kBlock} Dg[k][r] V[j0 + k][c] for c >= j0 + kBlock,
+// r < M (P and Dg column-major over r). The first group writes P, later ones
+// add to it. 128x128 output tiles, 8x8 per thread (two fp64 FMAs per LDS
+// value read), the contraction in chunks of 16 staged through LDS.
+constexpr int kUpd = 128;
+__global__ __launch_bounds__(256) void gptq_update_kernel(const double* __restrict__ Dg,
+                                                          const double* __restrict__ A, int64_t K,
+                                                          int64_t M, int64_t j0, int accumulate,
+                                                          double* __restrict__ P) {
+    __shared__ double sD[16][kUpd + 2];
+    __shared__ double sV[16][kUpd + 2];
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kUpd;
+    const int64_t c0 = j0 + kBlock + static_cast<int64_t>(blockIdx.y) * kUpd;
     const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
-    double acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < j0; k0 += 16) {
-        for (int e = threadIdx.x; e < 16 * 64; e += 256) {
-            const int k = e >> 6, c = e & 63;
-            sD[k][c] = (r0 + c < M) ? Dt[(k0 + k) * M + r0 + c] : 0.0;
-            sV[k][c] = A[(k0 + k) * K + j0 + c0 + c];
+    // Later groups add to the feedback so far, loaded first so that its
+    // latency overlaps the products.
+    double acc[8][8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const int64_t c = c0 + ty + 16 * v;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t r = r0 + tx + 16 * u;
+            acc[u][v] = (accumulate && c < K && r < M) ? P[c * M + r] : 0.0;
+        }
+    }
+    for (int k0 = 0; k0 < kBlock; k0 += 16) {
+        for (int e = threadIdx.x; e < 16 * kUpd; e += 256) {
+            const int k = e / kUpd, c = e % kUpd;
+            sD[k][c] = (r0 + c < M) ? Dg[static_cast<int64_t>(k0 + k) * M + r0 + c] : 0.0;
+            sV[k][c] = (c0 + c < K) ? A[(j0 + k0 + k) * K + c0 + c] : 0.0;
         }
         __syncthreads();
-#pragma unroll
+#pragma unroll 4
         for (int k = 0; k < 16; ++k) {
-            double a[4], b[4];
+            double a[8], b[8];
+            // rows tx + 16u and columns ty + 16v: consecutive lanes hold
+            // consecutive rows, which are contiguous in P
 #pragma unroll
-            for (int u = 0; u < 4; ++u) { a[u] = sD[k][ty * 4 + u]; b[u] = sV[k][tx * 4 + u]; }
+            for (int u = 0; u < 8; ++u) { a[u] = sD[k][tx + 16 * u]; b[u] = sV[k][ty + 16 * u]; }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 8; ++u)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+                for (int v = 0; v < 8; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t r = r0 + ty * 4 + u;
-        if (r >= M) continue;
+    for (int v = 0; v < 8; ++v) {
+        const int64_t c = c0 + ty + 16 * v;
+        if (c >= K) continue;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) P[static_cast<int64_t>(c0 + tx * 4 + v) * M + r] = acc[u][v];
+        for (int u = 0; u < 8; ++u) {
+            const int64_t r = r0 + tx + 16 * u;
+            if (r >= M) continue;
+            P[c * M + r] = acc[u][v];
+        }
     }
 }
 
@@ -250,7 +290,8 @@ __device__ __forceinline__ int nearest_code(double t, float s) {
 }
 
 // One 128-column group: one thread per row (64 rows per workgroup) rounds
-// the columns in order from t_j = w_j + P_j + sum_{i<j in group} d_i V_ij.
+// the columns in order from t_j = w_j + P_j + sum_{i<j in group} d_i V_ij,
+// P_j the feedback of the earlier groups, and writes the errors d to Dg.
 // The group's strictly upper block of V (packed, 8128 doubles) and the
 // workgroup's errors d (128 x 64 doubles) sit in LDS.
 template <int GRID, bool WBF16>
@@ -259,13 +300,14 @@ __global__ __launch_bounds__(64) void gptq_block_kernel(const void* __restrict__
                                                         const double* __restrict__ A,
                                                         const double* __restrict__ P, int has_p,
                                                         const float* __restrict__ scales,
-                                                        double* __restrict__ Dt,
+                                                        double* __restrict__ Dg,
                                                         uint8_t* __restrict__ codes) {
     __shared__ double Vp[kBlock * (kBlock - 1) / 2];
     __shared__ double dl[kBlock][64];
     const int lane = threadIdx.x;
-    for (int j = 1; j < kBlock; ++j)
-        for (int i = lane; i < j; i += 64) Vp[j * (j - 1) / 2 + i] = A[(j0 + i) * K + j0 + j];
+    // Row i of the block is contiguous in A: lanes read along it.
+    for (int i = 0; i < kBlock - 1; ++i)
+        for (int j = i + 1 + lane; j < kBlock; j += 64) Vp[j * (j - 1) / 2 + i] = A[(j0 + i) * K + j0 + j];
     __syncthreads();
     const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + lane;
     if (r >= M) return;
@@ -279,13 +321,13 @@ __global__ __launch_bounds__(64) void gptq_block_kernel(const void* __restrict__
         if constexpr (WBF16) w = static_cast<double>(bf16_lo(static_cast<const uint16_t*>(W)[r * K + j0 + j]));
         else w = static_cast<double>(static_cast<const float*>(W)[r * K + j0 + j]);
         double t = w;
-        if (has_p) t += P[static_cast<int64_t>(j) * M + r];
+        if (has_p) t += P[(j0 + j) * M + r];
         const double* vj = Vp + j * (j - 1) / 2;
         for (int i = 0; i < j; ++i) t = fma(dl[i][lane], vj[i], t);
         const int code = nearest_code<GRID>(t, s);
         const double d = w - static_cast<double>(s) * level_of<GRID>(code);
         dl[j][lane] = d;
-        Dt[(j0 + j) * M + r] = d;
+        Dg[static_cast<int64_t>(j) * M + r] = d;
         // Register index known only at run time: select through a switch-free
         // shift into the word the unrolled store loop below writes.
 #pragma unroll
@@ -332,12 +374,13 @@ hipError_t gptq_columns(const LayerDesc& d, const void* W, const GptqWorkspace& 
                         float* logits, float init_logit, hipStream_t st) {
     const int64_t M = d.rows, K = d.cols;
     for (int64_t j0 = 0; j0 < K; j0 += kBlock) {
-        if (j0 > 0) {
-            hipLaunchKernelGGL(gptq_gemm_kernel, dim3(cdivu(M, 64), kBlock / 64), dim3(256), 0, st,
-                               ws.Dt, ws.A, K, M, j0, ws.P);
-        }
         hipLaunchKernelGGL((gptq_block_kernel<GRID, WBF16>), dim3(cdivu(M, 64)), dim3(64), 0, st, W,
-                           M, K, j0, ws.A, ws.P, j0 > 0 ? 1 : 0, ws.scales, ws.Dt, codes);
+                           M, K, j0, ws.A, ws.P, j0 > 0 ? 1 : 0, ws.scales, ws.Dg, codes);
+        const int64_t later = K - j0 - kBlock;
+        if (later > 0) {
+            hipLaunchKernelGGL(gptq_update_kernel, dim3(cdivu(M, kUpd), cdivu(later, kUpd)), dim3(256),
+                               0, st, ws.Dg, ws.A, K, M, j0, j0 > 0 ? 1 : 0, ws.P);
+        }
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -362,8 +405,8 @@ GptqWorkspace gptq_carve(void* base, int64_t rows, int64_t cols) {
     GptqWorkspace ws{};
     ws.H32 = reinterpret_cast<float*>(p);  p += al(K * K * sizeof(float));
     ws.A = reinterpret_cast<double*>(p);   p += al(K * K * sizeof(double));
-    ws.Dt = reinterpret_cast<double*>(p);  p += al(M * K * sizeof(double));
-    ws.P = reinterpret_cast<double*>(p);   p += al(M * kBlock * sizeof(double));
+    ws.P = reinterpret_cast<double*>(p);   p += al(M * K * sizeof(double));
+    ws.Dg = reinterpret_cast<double*>(p);  p += al(M * kBlock * sizeof(double));
     ws.lambda = reinterpret_cast<double*>(p);
     return ws;
 }
@@ -376,11 +419,11 @@ hipError_t launch_gptq_factor(int64_t cols, float damp, const GptqWorkspace& ws,
     hipLaunchKernelGGL(reverse_damp_kernel, dim3(cdivu(K, 16), cdivu(K, 16)), dim3(256), 0, st,
                        ws.H32, K, ws.lambda, ws.A);
     for (int64_t p = 0; p < K; p += kPanel) {
-        hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, st, ws.A, K, p, info);
+        hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(kPanel), 0, st, ws.A, K, p, info);
         const int64_t rest = K - p - kPanel;
         if (rest > 0) {
             hipLaunchKernelGGL(trsm_kernel, dim3(cdivu(rest, 256)), dim3(256), 0, st, ws.A, K, p);
-            const int64_t T = (rest + 63) / 64;
+            const int64_t T = (rest + kSyrk - 1) / kSyrk;
             hipLaunchKernelGGL(syrk_kernel, dim3(static_cast<unsigned>(T * (T + 1) / 2)), dim3(256), 0,
                                st, ws.A, K, p);
         }

@@ -59,8 +59,8 @@ hipError_t launch_gram_f32(int64_t tokens, int64_t cols, const uint16_t* XT, flo
 struct GptqWorkspace {
     float* H32;           // [cols][cols] X^T X
     double* A;            // [cols][cols]: reversed Cholesky factor (lower), V (upper)
-    double* Dt;           // [cols][rows] rounding errors, column-major
-    double* P;            // [128][rows] feedback from earlier groups, column-major
+    double* P;            // [cols][rows] feedback of the finished groups, column-major
+    double* Dg;           // [128][rows] the current group's rounding errors, column-major
     double* lambda;       // damping added to the diagonal
     const float* scales;  // [rows][cols/128] group scales (the caller's output)
 };
