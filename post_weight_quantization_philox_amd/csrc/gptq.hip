@@ -20,14 +20,17 @@
 // panels: the diagonal block in LDS by one wave, a triangular solve for the
 // rows below, a symmetric rank-64 update of the trailing lower triangle); then
 // V_ij = R_ij / R_jj for i < j, written into the unused upper triangle of A;
-// then for every 128-column group: one thread per row runs the group's 128
-// columns sequentially (the group's block of V and the row's errors in LDS),
+// then for every 128-column group: eight lanes per row run the group's 128
+// columns sequentially (the group's block of V, the rows' w, w + P and
+// errors in LDS),
 // from targets that already hold the feedback of every earlier group; then
 // the group's errors D = W - Q are fed forward into all later columns at once
 // (P[:, later] += D V[group, later], an fp64 tiled product over the group's
 // 128 columns that covers the whole GPU). Group scales are the absmax scales of the
 // original weights (GPTQ's static groups), i.e. the round-to-nearest scales.
 #include <math.h>
+
+#include <algorithm>
 
 #include "gsq_internal.hpp"
 
@@ -289,55 +292,99 @@ __device__ __forceinline__ int nearest_code(double t, float s) {
     }
 }
 
-// One 128-column group: one thread per row (64 rows per workgroup) rounds
-// the columns in order from t_j = w_j + P_j + sum_{i<j in group} d_i V_ij,
-// P_j the feedback of the earlier groups, and writes the errors d to Dg.
-// The group's strictly upper block of V (packed, 8128 doubles) and the
-// workgroup's errors d (128 x 64 doubles) sit in LDS.
+// One 128-column group. kSplit lanes per row round the row's columns in
+// order from t_j = w_j + P_j + sum_{i<j in group} d_i V_ij, P_j the feedback
+// of the earlier groups, and write the errors d to Dg. Lane s of a row sums
+// the terms with i = s mod kSplit; a butterfly over the row's lanes adds the
+// partial sums (each step adds the same two values in every lane, so all
+// lanes hold the same t and take the same decision). A workgroup stages the
+// group's strictly upper block of V (packed, 8128 doubles) in LDS once and
+// then walks blocks of kRows rows, each with its w and w + P staged in LDS
+// by coalesced loads; lane j mod kSplit keeps d_j, the only lane reading it.
+constexpr int kSplit = 8;
+constexpr int kGroupThreads = 256;
+constexpr int kRows = kGroupThreads / kSplit;
 template <int GRID, bool WBF16>
-__global__ __launch_bounds__(64) void gptq_block_kernel(const void* __restrict__ W, int64_t M,
-                                                        int64_t K, int64_t j0,
-                                                        const double* __restrict__ A,
-                                                        const double* __restrict__ P, int has_p,
-                                                        const float* __restrict__ scales,
-                                                        double* __restrict__ Dg,
-                                                        uint8_t* __restrict__ codes) {
-    __shared__ double Vp[kBlock * (kBlock - 1) / 2];
-    __shared__ double dl[kBlock][64];
-    const int lane = threadIdx.x;
-    // Row i of the block is contiguous in A: lanes read along it.
+__global__ __launch_bounds__(kGroupThreads) void gptq_block_kernel(
+    const void* __restrict__ W, int64_t M, int64_t K, int64_t j0, const double* __restrict__ A,
+    const double* __restrict__ P, int has_p, const float* __restrict__ scales,
+    double* __restrict__ Dg, uint8_t* __restrict__ codes) {
+    // Padded by a row: the unrolled product loop may read past column j's
+    // entries (the values are masked, the addresses stay inside).
+    __shared__ double Vp[kBlock * (kBlock - 1) / 2 + kBlock];
+    __shared__ double dl[kBlock][kRows];
+    __shared__ double base[kBlock][kRows];   // w + P
+    __shared__ float wv[kBlock][kRows];      // w (bf16 or fp32 values)
+    __shared__ uint8_t cb[kRows][kBlock];    // the rows' codes
+    const int tid = threadIdx.x;
+    // Row i of the block is contiguous in A: threads read along it.
     for (int i = 0; i < kBlock - 1; ++i)
-        for (int j = i + 1 + lane; j < kBlock; j += 64) Vp[j * (j - 1) / 2 + i] = A[(j0 + i) * K + j0 + j];
-    __syncthreads();
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + lane;
-    if (r >= M) return;
-    const float s = scales[r * (K / kBlock) + j0 / kBlock];
-    uint32_t packed[kBlock / 4];
-#pragma unroll
-    for (int q = 0; q < kBlock / 4; ++q) packed[q] = 0;
+        for (int j = i + 1 + tid; j < kBlock; j += kGroupThreads)
+            Vp[j * (j - 1) / 2 + i] = A[(j0 + i) * K + j0 + j];
+    const int sub = tid % kSplit;
+    const int rl = tid / kSplit;
+    const int64_t nrb = (M + kRows - 1) / kRows;
+    for (int64_t rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
+        const int64_t rbase = rb * kRows;
+        // w along each row (contiguous in W), then P along each column
+        // (contiguous over rows).
+        for (int e = tid; e < kBlock * kRows; e += kGroupThreads) {
+            const int rr = e / kBlock, j = e % kBlock;
+            const int64_t r = rbase + rr;
+            float w = 0.0f;
+            if (r < M) {
+                if constexpr (WBF16) w = bf16_lo(static_cast<const uint16_t*>(W)[r * K + j0 + j]);
+                else w = static_cast<const float*>(W)[r * K + j0 + j];
+            }
+            wv[j][rr] = w;
+        }
+        __syncthreads();
+        for (int e = tid; e < kBlock * kRows; e += kGroupThreads) {
+            const int j = e / kRows, rr = e % kRows;
+            const int64_t r = rbase + rr;
+            double b = static_cast<double>(wv[j][rr]);
+            if (has_p && r < M) b += P[(j0 + j) * M + r];
+            base[j][rr] = b;
+        }
+        __syncthreads();
+        const int64_t r = rbase + rl;
+        if (r < M) {
+            const float s = scales[r * (K / kBlock) + j0 / kBlock];
 #pragma unroll 1
-    for (int j = 0; j < kBlock; ++j) {
-        double w;
-        if constexpr (WBF16) w = static_cast<double>(bf16_lo(static_cast<const uint16_t*>(W)[r * K + j0 + j]));
-        else w = static_cast<double>(static_cast<const float*>(W)[r * K + j0 + j]);
-        double t = w;
-        if (has_p) t += P[(j0 + j) * M + r];
-        const double* vj = Vp + j * (j - 1) / 2;
-        for (int i = 0; i < j; ++i) t = fma(dl[i][lane], vj[i], t);
-        const int code = nearest_code<GRID>(t, s);
-        const double d = w - static_cast<double>(s) * level_of<GRID>(code);
-        dl[j][lane] = d;
-        Dg[static_cast<int64_t>(j) * M + r] = d;
-        // Register index known only at run time: select through a switch-free
-        // shift into the word the unrolled store loop below writes.
+            for (int j = 0; j < kBlock; ++j) {
+                const double* vj = Vp + j * (j - 1) / 2;
+                // Fixed trip count (terms past j masked) so the LDS reads
+                // are issued ahead of the two product chains.
+                double p0 = 0.0, p1 = 0.0;
 #pragma unroll
-        for (int q = 0; q < kBlock / 4; ++q)
-            if (q == (j >> 2)) packed[q] |= static_cast<uint32_t>(code) << (8 * (j & 3));
+                for (int m = 0; m < kBlock / kSplit; m += 2) {
+                    const int i0 = sub + m * kSplit, i1 = i0 + kSplit;
+                    if (i0 < j) p0 = fma(dl[i0][rl], vj[i0], p0);
+                    if (i1 < j) p1 = fma(dl[i1][rl], vj[i1], p1);
+                }
+                double part = p0 + p1;
+#pragma unroll
+                for (int m = 1; m < kSplit; m <<= 1) part += __shfl_xor(part, m, kSplit);
+                const double t = base[j][rl] + part;
+                const int code = nearest_code<GRID>(t, s);
+                const double d = static_cast<double>(wv[j][rl]) - static_cast<double>(s) * level_of<GRID>(code);
+                if (sub == (j % kSplit)) dl[j][rl] = d;
+                if (sub == 0) {
+                    Dg[static_cast<int64_t>(j) * M + r] = d;
+                    cb[rl][j] = static_cast<uint8_t>(code);
+                }
+            }
+        }
+        __syncthreads();
+        // The rows' codes, 16 bytes per thread.
+        for (int e = tid; e < kRows * kBlock / 16; e += kGroupThreads) {
+            const int rr = e / (kBlock / 16), q = e % (kBlock / 16);
+            if (rbase + rr < M)
+                reinterpret_cast<uint4*>(codes + (rbase + rr) * K + j0)[q] =
+                    reinterpret_cast<const uint4*>(&cb[rr][0])[q];
+        }
+        __syncthreads();
     }
-    uint4* dst = reinterpret_cast<uint4*>(codes + r * K + j0);
-#pragma unroll
-    for (int q = 0; q < kBlock / 16; ++q)
-        dst[q] = make_uint4(packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]);
 }
 
 // Initial logits of the GPTQ codes (as the round-to-nearest warm start sets
@@ -374,7 +421,8 @@ hipError_t gptq_columns(const LayerDesc& d, const void* W, const GptqWorkspace& 
                         float* logits, float init_logit, hipStream_t st) {
     const int64_t M = d.rows, K = d.cols;
     for (int64_t j0 = 0; j0 < K; j0 += kBlock) {
-        hipLaunchKernelGGL((gptq_block_kernel<GRID, WBF16>), dim3(cdivu(M, 64)), dim3(64), 0, st, W,
+        const unsigned nb = static_cast<unsigned>(std::min<int64_t>(256, (M + kRows - 1) / kRows));
+        hipLaunchKernelGGL((gptq_block_kernel<GRID, WBF16>), dim3(nb), dim3(kGroupThreads), 0, st, W,
                            M, K, j0, ws.A, ws.P, j0 > 0 ? 1 : 0, ws.scales, ws.Dg, codes);
         const int64_t later = K - j0 - kBlock;
         if (later > 0) {
