@@ -51,10 +51,14 @@ def traffic_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
+# The sources the relax kernels (the dominant kernel's family) are built from.
+RELAX_SOURCES = ("gsq_device.hpp", "gsq_internal.hpp", "relax.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "post_weight_quantization_philox_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    for fn in RELAX_SOURCES:
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]
