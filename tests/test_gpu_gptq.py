@@ -72,7 +72,7 @@ def dev():
 
 
 @pytest.mark.parametrize("grid", GRIDS)
-@pytest.mark.parametrize("shape", [(64, 512, 256), (37, 384, 192)])
+@pytest.mark.parametrize("shape", [(64, 512, 256), (37, 384, 192), (40, 128, 192)])
 @pytest.mark.parametrize("w_bf16", [True, False])
 def test_gptq_parity(dev, grid, shape, w_bf16):
     M, K, N = shape
@@ -89,6 +89,22 @@ def test_gptq_parity(dev, grid, shape, w_bf16):
     # logits follow the GPU's own codes exactly as the warm start sets them
     np.testing.assert_array_equal(lg.view(np.uint32),
                                   ogsq._logits_from_codes(c, W, grid, 2.0).view(np.uint32))
+
+
+def test_gptq_more_rows_than_one_pass(dev):
+    """More rows than one pass of the group kernel's workgroups covers (256
+    workgroups of 32 rows), with a ragged last block: every row against the
+    oracle."""
+    M, K, N = 8200, 256, 192
+    d = synthetic.small_layer(M, K, N, seed=21)
+    W, ws, s, c, lg, info = _run(d, oracle.GRID_INT2, dev)
+    assert info == 0
+    s_ref, c_ref, _, T_ref = oracle.gptq(W, d["X"], oracle.GRID_INT2)
+    np.testing.assert_array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    bad = _compare_rows(c, c_ref, T_ref, s_ref, oracle.GRID_INT2)
+    report("gptq 8200 rows", rows_split_at_a_tie=bad,
+           codes_moved_vs_rtn=float(np.mean(c_ref != oracle.init_rtn(W, 0)[1])))
+    assert bad <= max(1, M // 20)
 
 
 def test_gptq_factor_matches_cholesky(dev):
