@@ -320,7 +320,7 @@ def main():
         kernels = {
             "relax_fwd": {"ms": fwd_ms, "GB/s": FWD_BYTES_PER_COORD * coords / fwd_ms / 1e6},
             "recon_loss_grad": {"ms": rec_ms, "TFLOP/s": gemm_flops / rec_ms / 1e9,
-                                "note": "two bf16 GEMMs (2NMK flops each) + loss finalize"},
+                                "note": "two bf16 GEMMs (2NMK flops each); GEMM2's first workgroup sums the loss"},
             "relax_bwd_lion": {"ms": bwd_ms, "GB/s": BWD_BYTES_PER_COORD * coords / bwd_ms / 1e6},
         }
         per_launch = {"relax_fwd": fwd_ms, "recon_loss_grad": rec_ms / n_gemm,
@@ -330,7 +330,7 @@ def main():
         elapsed, rec_ms, fus_ms = time_fused(solver, taus, args.warmup, args.steps, stream)
         kernels = {
             "recon_loss_grad": {"ms": rec_ms, "TFLOP/s": gemm_flops / rec_ms / 1e9,
-                                "note": "two bf16 GEMMs (2NMK flops each) + loss finalize"},
+                                "note": "two bf16 GEMMs (2NMK flops each); GEMM2's first workgroup sums the loss"},
             "relax_bwd_lion_fwd": {"ms": fus_ms,
                                    "GB/s": FUSED_BYTES_PER_COORD * coords / fus_ms / 1e6,
                                    "note": "backward + Lion of step t and forward of step t+1"},
@@ -340,9 +340,8 @@ def main():
     loss = float(solver.loss.item())
     ms_per_step = elapsed * 1e3 / args.steps
 
-    # Dominant single kernel: the recon call is two GEMM launches per expert
-    # (equal flops) plus a few-microsecond loss finalize, so each GEMM launch
-    # is weighed at its share of the call.
+    # Dominant single kernel: the recon call is two GEMM launches of equal
+    # flops, so each GEMM launch is weighed at its share of the call.
     dominant = max(per_launch, key=per_launch.get)
     if dominant == "recon_loss_grad":
         ach = kernels[dominant]["TFLOP/s"]

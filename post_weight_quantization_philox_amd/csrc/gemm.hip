@@ -59,6 +59,12 @@ struct GemmArgs {
     float* partials;   // EPI_BF16_LOSS, EPI_F32_GRAM: one float per workgroup
     const uint16_t* D; // EPI_F32_GRAM: bf16 [I][ldd] paired with the output
     int64_t ldd;
+    // Optional: workgroup 0 first sums fin_n loss partials of an earlier
+    // launch into *fin_loss (the same order as loss_finalize_kernel), which
+    // saves that launch.
+    const float* fin_partials;
+    int fin_n;
+    double* fin_loss;
 };
 
 // Experts of one grouped launch (at most kMaxGroups). Expert e of the launch
@@ -169,6 +175,18 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     __shared__ uint4 sA1[BM * kChunks];
     __shared__ uint4 sB1[BN * kChunks];
 
+    if (g.fin_loss != nullptr && blockIdx.x == 0) {
+        __shared__ double fred[NT];
+        double fs = 0.0;
+        for (int i = threadIdx.x; i < g.fin_n; i += NT) fs += static_cast<double>(g.fin_partials[i]);
+        fred[threadIdx.x] = fs;
+        __syncthreads();
+        for (int w = NT / 2; w >= 1; w >>= 1) {
+            if (static_cast<int>(threadIdx.x) < w) fred[threadIdx.x] += fred[threadIdx.x + w];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) *g.fin_loss = fred[0];
+    }
     int local = logical_wg();
     if constexpr (GROUPED) local = resolve(eb, local, g);
     int ti, tj;
@@ -472,9 +490,11 @@ inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b)
 template <int EPI>
 hipError_t run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int I, int J,
                     int Rd, void* C, int64_t ldc, float alpha, float* partials, hipStream_t st,
-                    const uint16_t* D = nullptr, int64_t ldd = 0) {
-    GemmArgs g;
+                    const uint16_t* D = nullptr, int64_t ldd = 0,
+                    const float* fin_partials = nullptr, int fin_n = 0, double* fin_loss = nullptr) {
+    GemmArgs g{};
     g.D = D; g.ldd = ldd;
+    g.fin_partials = fin_partials; g.fin_n = fin_n; g.fin_loss = fin_loss;
     g.A = A; g.B = B; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
     g.I = I; g.J = J; g.Rd = Rd;
     const int64_t ab = static_cast<int64_t>(I) * lda * 2, bb = static_cast<int64_t>(J) * ldb * 2;
@@ -499,7 +519,8 @@ hipError_t run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t l
 hipError_t run_expert_batch(int e0, int e1, const int64_t* tok_offsets, int64_t rpe, int64_t cols,
                             const uint16_t* X, const uint16_t* XT, const uint16_t* dW,
                             float* partials, uint16_t* RT, float* G, hipStream_t st,
-                            size_t* n_partials) {
+                            size_t* n_partials, const float* fin_base = nullptr,
+                            size_t fin_prior = 0, double* fin_loss = nullptr) {
     ExpertBatch eb{};
     eb.n = e1 - e0;
     eb.rpe = static_cast<int>(rpe);
@@ -540,6 +561,12 @@ hipError_t run_expert_batch(int e0, int e1, const int64_t* tok_offsets, int64_t 
     for (int e = 0; e <= eb.n; ++e) eb.wg0[e] = wg0_2[e];
     g.alpha = 2.0f;
     g.partials = nullptr;
+    if (fin_loss != nullptr) {
+        // The loss over every chunk's partials, this chunk's included.
+        g.fin_partials = fin_base;
+        g.fin_n = static_cast<int>(fin_prior + *n_partials);
+        g.fin_loss = fin_loss;
+    }
     hipLaunchKernelGGL((gemm_nt_kernel<EPI_F32_SCALED, true>), dim3(wg2), dim3(NT), 0, st, g, eb);
     return hipGetLastError();
 }
@@ -573,9 +600,12 @@ hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t r
                                           1.0f, partials, st);
             if (err == hipSuccess) {
                 slot = static_cast<size_t>(cdiv(rows_per_expert, BM)) * cdiv(ne, BN);
+                // GEMM2's first workgroup also sums GEMM1's loss partials.
                 err = run_gemm<EPI_F32_SCALED>(RT, ne, XT, ne, static_cast<int>(rows_per_expert),
                                                static_cast<int>(cols), static_cast<int>(ne), G,
-                                               cols, 2.0f, nullptr, st);
+                                               cols, 2.0f, nullptr, st, nullptr, 0, partials,
+                                               static_cast<int>(slot), loss);
+                return err;
             }
         }
     } else {
@@ -584,10 +614,14 @@ hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t r
         for (int e0 = 0; e0 < n_experts && err == hipSuccess; e0 += kMaxGroups) {
             const int e1 = e0 + kMaxGroups < n_experts ? e0 + kMaxGroups : n_experts;
             size_t np = 0;
+            // The last chunk's GEMM2 also sums every chunk's loss partials.
+            const bool last = e1 == n_experts;
             err = run_expert_batch(e0, e1, tok_offsets, rows_per_expert, cols, X, XT, dW,
-                                   partials + slot, RT, G, st, &np);
+                                   partials + slot, RT, G, st, &np, partials, slot,
+                                   last ? loss : nullptr);
             slot += np;
         }
+        return err;
     }
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(256), 0, st, partials,
