@@ -231,7 +231,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the oracle sample (default: about 1.4e11 flops of products)")
-    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="synthetic layer: linear512_int2, qproj4096_int2 (default), "
+                         "downproj4096x14336_ternary, gateproj28672x8192_int3local, "
+                         "gateproj28672x8192_int3full, moe64x2048x7168_int2")
     ap.add_argument("--block", action="store_true",
                     help="time GSQ's staged schedule over one Llama-3.1-8B-shaped decoder block "
                          "(random weights, 4096 tokens) instead of the per-layer step")
