@@ -4,7 +4,9 @@
 // contraction index r contiguous in both operands.
 //   GEMM1  R^T = dW X^T      A = dW [M][K],   B = X   [N][K]  -> R^T [M][N] bf16,
 //                            plus the per-tile partial sum of R^2 (the loss);
-//   GEMM2  G   = 2 R^T X     A = R^T [M][N],  B = X^T [K][N]  -> G [M][K] fp32.
+//   GEMM2  G   = 2 R^T X     A = R^T [M][N],  B = X^T [K][N]  -> G [M][K] fp32;
+//                            its first workgroup also sums GEMM1's partials
+//                            into the loss (fixed order, fp64).
 // For a batch of experts each product is one grouped launch over all the
 // experts' tiles. The same kernel also forms the Gram matrix H = X^T X (bf16
 // or fp32 output), the Gram-form step G = 2 dW H with the loss sum dW * dW H
