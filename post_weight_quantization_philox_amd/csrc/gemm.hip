@@ -22,7 +22,9 @@
 // conflicts. Workgroups are renumbered so that consecutive tiles share an XCD
 // (the dispatcher deals workgroups round-robin over the 8 XCDs) and tiles are
 // ordered in groups of 4 tile-rows, which keeps each XCD's A and B panels in
-// its own L2.
+// its own L2. A product that does not fill its last round of 256 tiles runs
+// whole rounds of full tiles on a column or row block and the rest as 256x128
+// tiles (same kernel, waves of 128x64), with unchanged summation order.
 #include <type_traits>
 
 #include "gsq_internal.hpp"
@@ -143,14 +145,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 // physical chunks, which makes the access conflict-free.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// One K-step of one operand tile: 256 rows x 64 bf16 = 32 KiB, written by
-// direct global->LDS loads. Wave w, load q fills tile rows R0..R0+7 with
+// One K-step of one operand tile: 32 Q rows x 64 bf16 (32 KiB for 256 rows),
+// written by direct global->LDS loads. Wave w, load q fills tile rows R0..R0+7 with
 // R0 = 8*(4q + w); lane l lands at LDS row R0 + l/8, physical chunk l%8, and
 // therefore fetches logical chunk (l%8) ^ swz(row) of its row.
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[8], uint32_t koff,
+template <int Q>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, const uint32_t* off, uint32_t koff,
                                          uint4* tile, int wave) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < Q; ++q) {
         const int r0 = 8 * (4 * q + wave);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + r0 * kChunks), 16,
                                                  off[q], koff, 0, 0);
@@ -169,11 +172,19 @@ __device__ __forceinline__ void bar() {
 }
 
 // GROUPED: one launch over the experts of `eb` (its product replaces the
-// operand fields of g); otherwise g is one product and eb is unused.
-template <int EPI, bool GROUPED>
+// operand fields of g); otherwise g is one product and eb is unused. TBN is
+// the tile width: 256, or 128 (each wave 128x64) for the tiles of a launch's
+// last, partial round, which then finish in about half the time.
+template <int EPI, bool GROUPED, int TBN>
 __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb) {
+    static_assert(TBN == 256 || TBN == 128, "tile width 256 or 128");
+    static_assert(!GROUPED || TBN == BN, "expert batches use the full tile");
+    static_assert(EPI != EPI_F32_GRAM || TBN == BN, "the Gram form uses the full tile");
+    constexpr int WN = TBN / 2;      // wave tile width
+    constexpr int NB = WN / 32;      // 32-column MFMA blocks per wave
+    constexpr int QB = TBN / 32;     // DMA row groups of the B tile
     __shared__ uint4 sA0[BM * kChunks];
-    __shared__ uint4 sB0[BN * kChunks];
+    __shared__ uint4 sB0[BN * kChunks];   // a 128-wide tile uses the first half
     __shared__ uint4 sA1[BM * kChunks];
     __shared__ uint4 sB1[BN * kChunks];
 
@@ -193,7 +204,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     if constexpr (GROUPED) local = resolve(eb, local, g);
     int ti, tj;
     tile_of(local, g.tiles_i, g.tiles_j, ti, tj);
-    const int i0 = ti * BM, j0 = tj * BN;
+    const int i0 = ti * BM, j0 = tj * TBN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // Wave index as a scalar: LDS destinations of the DMA loads (the M0
@@ -208,21 +219,22 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(g.B), 0, g.b_bytes, 0x00020000);
     const int lrow = lane >> 3;
-    uint32_t oa[8], ob[8];
+    uint32_t oa[8], ob[8];   // ob: the first QB entries are used
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int row = 8 * (4 * q + wave) + lrow;
         const int lch = (lane & 7) ^ swz(row);
         const int rowa = i0 + row, rowb = j0 + row;
         oa[q] = rowa < g.I ? static_cast<uint32_t>((static_cast<int64_t>(rowa) * g.lda + lch * 8) * 2) : kOob;
-        ob[q] = rowb < g.J ? static_cast<uint32_t>((static_cast<int64_t>(rowb) * g.ldb + lch * 8) * 2) : kOob;
+        if (q < QB)
+            ob[q] = rowb < g.J ? static_cast<uint32_t>((static_cast<int64_t>(rowb) * g.ldb + lch * 8) * 2) : kOob;
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][NB];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
@@ -233,37 +245,49 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     const int fhalf = lane >> 5;
     const int fsw = swz(frow);
     const int rowA = wi * 128 + frow;
-    const int rowB = wj * 128 + frow;
+    const int rowB = wj * WN + frow;
 
     // Fragment registers: one slot per 16-wide slice of the K-step (slice kk
     // always lives in slot kk), fetched two slices ahead of its MFMAs.
-    bf16x8 fa[4][4], fb[4][4];
+    bf16x8 fa[4][4], fb[4][NB];
     auto read_a = [&](const uint4* t, int kk, int b) {
         return __builtin_bit_cast(bf16x8, t[(rowA + 32 * b) * kChunks + ((2 * kk + fhalf) ^ fsw)]);
     };
     auto read_b = [&](const uint4* t, int kk, int b) {
         return __builtin_bit_cast(bf16x8, t[(rowB + 32 * b) * kChunks + ((2 * kk + fhalf) ^ fsw)]);
     };
-    // DMA load d (0..15) of a K-step: A loads q = 0..7, then B.
+    // DMA load d (0..15) of a K-step: A loads q = 0..7, then B's QB loads
+    // (a 128-wide tile has 4: its last four slots load nothing).
     auto dma1 = [&](int d, uint32_t koff, uint4* nA, uint4* nB) {
         const int q = d & 7;
         const int r0 = 8 * (4 * q + wave);
         if (d < 8)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rs, (lds_void*)(nA + r0 * kChunks), 16,
                                                      oa[q], koff, 0, 0);
-        else
+        else if (q < QB)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rs, (lds_void*)(nB + r0 * kChunks), 16,
                                                      ob[q], koff, 0, 0);
     };
     // Two of the eight fragment reads of slice kk into its slot, in the
     // order its MFMAs consume them: B blocks 0-1, B 2-3, A 0-1, A 2-3.
+    // With two B blocks (128-wide tile): B 0-1, A 0-1, A 2-3, nothing.
     auto fetch2 = [&](const uint4* tA, const uint4* tB, int kk, int part) {
-        if (part < 2) {
-            fb[kk][2 * part] = read_b(tB, kk, 2 * part);
-            fb[kk][2 * part + 1] = read_b(tB, kk, 2 * part + 1);
+        if constexpr (NB == 4) {
+            if (part < 2) {
+                fb[kk][2 * part] = read_b(tB, kk, 2 * part);
+                fb[kk][2 * part + 1] = read_b(tB, kk, 2 * part + 1);
+            } else {
+                fa[kk][2 * part - 4] = read_a(tA, kk, 2 * part - 4);
+                fa[kk][2 * part - 3] = read_a(tA, kk, 2 * part - 3);
+            }
         } else {
-            fa[kk][2 * part - 4] = read_a(tA, kk, 2 * part - 4);
-            fa[kk][2 * part - 3] = read_a(tA, kk, 2 * part - 3);
+            if (part == 0) {
+                fb[kk][0] = read_b(tB, kk, 0);
+                fb[kk][1] = read_b(tB, kk, 1);
+            } else if (part < 3) {
+                fa[kk][2 * part - 2] = read_a(tA, kk, 2 * part - 2);
+                fa[kk][2 * part - 1] = read_a(tA, kk, 2 * part - 1);
+            }
         }
     };
 
@@ -300,7 +324,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
                     }
                 }
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
+                for (int b = 0; b < NB; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][a], fb[kk][b],
                                                                         acc[a][b], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -313,13 +337,14 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     // An expert without tokens has an empty contraction: its output is zero.
     if (nk > 0) {
         // Prologue: step 0 (waited for) and step 1 in flight; slices 0-1 fetched.
-        dma_tile(ra_rs, oa, 0, sA0, wave);
-        dma_tile(rb_rs, ob, 0, sB0, wave);
+        dma_tile<8>(ra_rs, oa, 0, sA0, wave);
+        dma_tile<QB>(rb_rs, ob, 0, sB0, wave);
         if (nk > 1) {
             wait_dma();
-            dma_tile(ra_rs, oa, kStep, sA1, wave);
-            dma_tile(rb_rs, ob, kStep, sB1, wave);
-            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            dma_tile<8>(ra_rs, oa, kStep, sA1, wave);
+            dma_tile<QB>(rb_rs, ob, kStep, sB1, wave);
+            if constexpr (QB == 8) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
         } else {
             wait_dma();
         }
@@ -356,12 +381,12 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     // lane reads back 8 (bf16 output) or 4 (fp32 output) consecutive values of
     // one row and stores them as one 16-byte vector. N and K are multiples of
     // 8, so a vector is entirely inside or outside the matrix.
-    constexpr int kSlab = 128 + 4;      // padded row: the two half-waves' rows
+    constexpr int kSlab = WN + 4;      // padded row: the two half-waves' rows
                                         // start 16 bytes apart in the banks
     // One 32 KiB buffer per wave.
     float* slab = reinterpret_cast<float*>(wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1);
     const int grow0 = i0 + wi * 128;
-    const int gcol0 = j0 + wj * 128;
+    const int gcol0 = j0 + wj * WN;
     float lsum = 0.0f;
     // Gram form: the dW values a slab pairs with, loaded one slab ahead so
     // their latency overlaps the previous slab's work (zero outside the
@@ -384,7 +409,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
             if (a + 1 < 4) load_dv(a + 1, dv[(a + 1) & 1]);
         }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < NB; ++b) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = 8 * (r >> 2) + 4 * fhalf + (r & 3);
@@ -394,10 +419,11 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
         __syncthreads();
         if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_BF16) {
             // 16 lanes per 128-value row: 8 values -> one 16-byte bf16 store.
+            constexpr int LPR = WN / 8;   // lanes per row
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < 32 * LPR / 64; ++t) {
                 const int c = lane + 64 * t;
-                const int row = c >> 4, col = (c & 15) * 8;
+                const int row = c / LPR, col = (c % LPR) * 8;
                 const float4 v0 = *reinterpret_cast<const float4*>(slab + row * kSlab + col);
                 const float4 v1 = *reinterpret_cast<const float4*>(slab + row * kSlab + col + 4);
                 const int grow = grow0 + a * 32 + row, gcol = gcol0 + col;
@@ -418,10 +444,11 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
         } else {
             // 32 lanes per 128-value row: each store instruction writes two
             // whole 512-byte rows.
+            constexpr int LPR = WN / 4;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int t = 0; t < 32 * LPR / 64; ++t) {
                 const int c = lane + 64 * t;
-                const int row = c >> 5, col = (c & 31) * 4;
+                const int row = c / LPR, col = (c % LPR) * 4;
                 const float4 v = *reinterpret_cast<const float4*>(slab + row * kSlab + col);
                 const int grow = grow0 + a * 32 + row, gcol = gcol0 + col;
                 if (grow < g.I && gcol < g.J) {
@@ -489,6 +516,65 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
 
 inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
+// One launch of the product over rows [r0, r0 + I) and columns [c0, c0 + J)
+// of the full product, tiles TBN wide.
+template <int EPI, int TBN>
+void launch_part(GemmArgs g, int r0, int c0, int I, int J, float* partials, hipStream_t st) {
+    g.A += static_cast<int64_t>(r0) * g.lda;
+    g.B += static_cast<int64_t>(c0) * g.ldb;
+    if (g.D) g.D += static_cast<int64_t>(r0) * g.ldd + c0;
+    g.I = I; g.J = J;
+    g.a_bytes = static_cast<int>(static_cast<int64_t>(I) * g.lda * 2);
+    g.b_bytes = static_cast<int>(static_cast<int64_t>(J) * g.ldb * 2);
+    constexpr int esz = (EPI == EPI_BF16_LOSS || EPI == EPI_BF16) ? 2 : 4;
+    g.C = static_cast<char*>(g.C) + (static_cast<int64_t>(r0) * g.ldc + c0) * esz;
+    g.partials = partials;
+    g.tiles_i = cdiv(I, BM); g.tiles_j = cdiv(J, TBN);
+    ExpertBatch none{};
+    hipLaunchKernelGGL((gemm_nt_kernel<EPI, false, TBN>), dim3(g.tiles_i * g.tiles_j), dim3(NT), 0,
+                       st, g, none);
+}
+
+constexpr int kCUs = 256;   // MI355X compute units: one workgroup each per round
+
+// How one product of ti x tj full tiles is launched. A partial last round
+// leaves compute units idle while its tiles run, so whole rounds of full tiles
+// go to a column block (COLS) or a row block (ROWS) of `at` tiles, and the rest
+// of the product to 128-wide tiles, which finish in about half the time; a
+// product under half a round uses 128-wide tiles throughout (NARROW).
+struct Split {
+    enum Kind { FULL, NARROW, COLS, ROWS } kind;
+    int at;
+};
+
+Split plan_split(int I, int J) {
+    const int ti = cdiv(I, BM), tj = cdiv(J, BN), T = ti * tj;
+    if (T % kCUs == 0) return {Split::FULL, 0};
+    if (T * 2 <= kCUs) return {Split::NARROW, 0};
+    auto gcd = [](int a, int b) { while (b) { const int t = a % b; a = b; b = t; } return a; };
+    const int n0 = kCUs / gcd(ti, kCUs), jm = (tj / n0) * n0;
+    if (jm > 0 && jm < tj && ti * (tj - jm) * 2 <= kCUs) return {Split::COLS, jm};
+    const int m0 = kCUs / gcd(tj, kCUs), im = (ti / m0) * m0;
+    if (im > 0 && im < ti && (ti - im) * tj * 2 <= kCUs) return {Split::ROWS, im};
+    return {Split::FULL, 0};
+}
+
+// Workgroups (and loss partials) of one product of I x J outputs.
+int product_workgroups(int I, int J) {
+    const Split sp = plan_split(I, J);
+    const int ti = cdiv(I, BM), tj = cdiv(J, BN);
+    switch (sp.kind) {
+        case Split::NARROW: return ti * cdiv(J, 128);
+        case Split::COLS: return ti * sp.at + ti * cdiv(J - sp.at * BN, 128);
+        case Split::ROWS: return sp.at * tj + (ti - sp.at) * cdiv(J, 128);
+        default: return ti * tj;
+    }
+}
+
+// C[I][J] = alpha * A[I][Rd] B[J][Rd]^T (EPI selects the output form). With
+// fin_loss set, the first workgroup also sums fin_n earlier loss partials
+// into *fin_loss; partials (loss epilogues) receive product_workgroups(I, J)
+// values.
 template <int EPI>
 hipError_t run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int I, int J,
                     int Rd, void* C, int64_t ldc, float alpha, float* partials, hipStream_t st,
@@ -505,13 +591,32 @@ hipError_t run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t l
     if (Rd <= 0 || Rd % BK != 0 || ab > static_cast<int64_t>(kOob) - 2 * static_cast<int64_t>(Rd) ||
         bb > static_cast<int64_t>(kOob) - 2 * static_cast<int64_t>(Rd))
         return hipErrorInvalidValue;
-    g.a_bytes = static_cast<int>(ab);
-    g.b_bytes = static_cast<int>(bb);
-    g.tiles_i = cdiv(I, BM); g.tiles_j = cdiv(J, BN);
-    g.C = C; g.alpha = alpha; g.partials = partials;
-    const int nwg = g.tiles_i * g.tiles_j;
-    ExpertBatch none{};
-    hipLaunchKernelGGL((gemm_nt_kernel<EPI, false>), dim3(nwg), dim3(NT), 0, st, g, none);
+    g.C = C; g.alpha = alpha;
+    // The Gram form keeps full tiles (its products are whole rounds here).
+    const Split sp = EPI == EPI_F32_GRAM ? Split{Split::FULL, 0} : plan_split(I, J);
+    const int ti = cdiv(I, BM), tj = cdiv(J, BN);
+    float* tail_partials = nullptr;
+    switch (sp.kind) {
+        case Split::NARROW:
+            if constexpr (EPI != EPI_F32_GRAM) launch_part<EPI, 128>(g, 0, 0, I, J, partials, st);
+            break;
+        case Split::COLS:
+            launch_part<EPI, BN>(g, 0, 0, I, sp.at * BN, partials, st);
+            g.fin_loss = nullptr;
+            if (partials) tail_partials = partials + ti * sp.at;
+            if constexpr (EPI != EPI_F32_GRAM)
+                launch_part<EPI, 128>(g, 0, sp.at * BN, I, J - sp.at * BN, tail_partials, st);
+            break;
+        case Split::ROWS:
+            launch_part<EPI, BN>(g, 0, 0, sp.at * BM, J, partials, st);
+            g.fin_loss = nullptr;
+            if (partials) tail_partials = partials + sp.at * tj;
+            if constexpr (EPI != EPI_F32_GRAM)
+                launch_part<EPI, 128>(g, sp.at * BM, 0, I - sp.at * BM, J, tail_partials, st);
+            break;
+        default:
+            launch_part<EPI, BN>(g, 0, 0, I, J, partials, st);
+    }
     return hipGetLastError();
 }
 
@@ -555,7 +660,7 @@ hipError_t run_expert_batch(int e0, int e1, const int64_t* tok_offsets, int64_t 
     *n_partials = static_cast<size_t>(wg1);
     if (wg1 > 0) {
         eb.stage = 0;
-        hipLaunchKernelGGL((gemm_nt_kernel<EPI_BF16_LOSS, true>), dim3(wg1), dim3(NT), 0, st, g, eb);
+        hipLaunchKernelGGL((gemm_nt_kernel<EPI_BF16_LOSS, true, BN>), dim3(wg1), dim3(NT), 0, st, g, eb);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -569,7 +674,7 @@ hipError_t run_expert_batch(int e0, int e1, const int64_t* tok_offsets, int64_t 
         g.fin_n = static_cast<int>(fin_prior + *n_partials);
         g.fin_loss = fin_loss;
     }
-    hipLaunchKernelGGL((gemm_nt_kernel<EPI_F32_SCALED, true>), dim3(wg2), dim3(NT), 0, st, g, eb);
+    hipLaunchKernelGGL((gemm_nt_kernel<EPI_F32_SCALED, true, BN>), dim3(wg2), dim3(NT), 0, st, g, eb);
     return hipGetLastError();
 }
 
@@ -579,7 +684,12 @@ size_t recon_partials(int32_t n_experts, const int64_t* tok_offsets, int64_t row
     size_t n = 0;
     for (int e = 0; e < n_experts; ++e) {
         const int64_t ne = tok_offsets[e + 1] - tok_offsets[e];
-        if (ne > 0) n += static_cast<size_t>(cdiv(rows_per_expert, BM)) * cdiv(ne, BN);
+        if (ne == 0) continue;
+        // A dense layer's GEMM1 may split its last round (product_workgroups);
+        // expert batches launch whole tiles.
+        n += n_experts == 1 ? static_cast<size_t>(product_workgroups(static_cast<int>(rows_per_expert),
+                                                                     static_cast<int>(ne)))
+                            : static_cast<size_t>(cdiv(rows_per_expert, BM)) * cdiv(ne, BN);
     }
     return n;
 }
@@ -601,7 +711,8 @@ hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t r
                                           static_cast<int>(ne), static_cast<int>(cols), RT, ne,
                                           1.0f, partials, st);
             if (err == hipSuccess) {
-                slot = static_cast<size_t>(cdiv(rows_per_expert, BM)) * cdiv(ne, BN);
+                slot = static_cast<size_t>(product_workgroups(static_cast<int>(rows_per_expert),
+                                                              static_cast<int>(ne)));
                 // GEMM2's first workgroup also sums GEMM1's loss partials.
                 err = run_gemm<EPI_F32_SCALED>(RT, ne, XT, ne, static_cast<int>(rows_per_expert),
                                                static_cast<int>(cols), static_cast<int>(ne), G,

@@ -33,11 +33,16 @@ def _close_ulp(got, ref, ulps=1):
     assert np.all(np.abs(got - ref) <= ulps * bf16_ulp(ref) + 1e-30)
 
 
-def test_matmul_nt(dev):
+@pytest.mark.parametrize("I,J,R", [
+    (200, 136, 192),       # under half a round: 128-wide tiles throughout
+    (4096, 4096, 64),      # exactly one round of 256x256 tiles
+    (4000, 5000, 64),      # a column block of whole rounds + a ragged 128-wide tail
+    (5000, 4000, 64),      # a row block of whole rounds + a ragged 128-wide tail
+])
+def test_matmul_nt(dev, I, J, R):
     import torch
     import post_weight_quantization_philox_amd as g
-    rng = np.random.default_rng(0)
-    I, J, R = 200, 136, 192
+    rng = np.random.default_rng(I + J + R)
     a_bits, A = _rand_bf16(rng, (I, R))
     b_bits, B = _rand_bf16(rng, (J, R))
     C = torch.empty((I, J), dtype=torch.bfloat16, device=dev)

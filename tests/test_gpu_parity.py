@@ -226,6 +226,13 @@ _OFFS67 = [0] + np.cumsum(np.random.default_rng(67).choice([0, 64, 128], 67)).to
     (300, 192, 384, None),            # ragged rows, partial tiles
     (3 * 256, 320, 256, [0, 128, 128, 320]),   # three experts, one with no tokens
     (67 * 32, _OFFS67[-1], 256, _OFFS67),      # two grouped launches per product
+    # Products over more than one round of 256 tiles that do not fill the
+    # last round: whole rounds of 256x256 tiles on a column or row block, the
+    # rest in 256x128 tiles (ragged where the sizes are).
+    (4000, 64, 5120, None),           # G: column block + 128-wide tail
+    (5000, 64, 4096, None),           # G: row block + 128-wide ragged tail
+    (4000, 5056, 128, None),          # R^T: column block + ragged tail
+    (5000, 4096, 128, None),          # R^T: row block + ragged tail
 ])
 def test_recon_loss_grad(dev, M, N, K, offs):
     import torch
