@@ -204,10 +204,11 @@ def block_bench(args, dev):
     w["g_mlp"] = torch.ones(cfg.hidden, device=dev)
     x = torch.randn((4096, cfg.hidden), generator=gen, device=dev).to(torch.bfloat16)
     lion = g.GsqLion.make(lr_logit=1e-3, lr_scale=1e-5)
-    staged_quantize(cfg, w, x[:256], g.GRID_INT2, 2, lion)      # warm the code paths
+    staged_quantize(cfg, w, x[:256], g.GRID_INT2, 2, lion, recon=args.block_recon)   # warm up
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    _, info = staged_quantize(cfg, w, x, g.GRID_INT2, args.block_steps, lion)
+    _, info = staged_quantize(cfg, w, x, g.GRID_INT2, args.block_steps, lion,
+                              recon=args.block_recon)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     n_w = sum(o * i for o, i in cfg.shapes().values())
@@ -218,8 +219,8 @@ def block_bench(args, dev):
         "dtype": "f32 relax+Lion, bf16 MFMA (fp32 accumulate), bf16 block forward",
         "config": {"workload": "Llama-3.1-8B-shaped decoder block (hidden 4096, 32 heads, 8 kv "
                                "heads, MLP 14336), random weights, 4096 tokens N(0,1), 2-bit grid",
-                   "weights": n_w},
-        "stages": {k: {"seconds": v["seconds"]} for k, v in info.items()},
+                   "weights": n_w, "recon": args.block_recon},
+        "stages": {k: {"seconds": v["seconds"], "recon": v["recon"]} for k, v in info.items()},
     }), flush=True)
 
 
@@ -239,6 +240,9 @@ def main():
                     help="time GSQ's staged schedule over one Llama-3.1-8B-shaped decoder block "
                          "(random weights, 4096 tokens) instead of the per-layer step")
     ap.add_argument("--block-steps", type=int, default=50)
+    ap.add_argument("--block-recon", default="auto", choices=("direct", "gram", "auto"),
+                    help="reconstruction form per layer in --block: the two direct products, "
+                         "the Gram form, or whichever needs fewer flops (default)")
     ap.add_argument("--init", choices=("rtn", "gptq"), default="rtn",
                     help="warm start; GPTQ's set-up time is reported under 'setup' (not in the step)")
     ap.add_argument("--unfused", action="store_true",

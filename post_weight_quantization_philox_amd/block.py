@@ -111,24 +111,41 @@ def forward(cfg: BlockConfig, w: dict, x: torch.Tensor) -> dict:
     return {"out": out, "x_attn": xa, "x_o": ao, "h": hres, "x_mlp": xm, "x_down": act}
 
 
+def recon_form(recon: str, cols: int, tokens: int) -> str:
+    """The reconstruction form a layer uses. ``"auto"`` takes the Gram form
+    (H = X^T X once, then one product of 2 rows cols^2 flops per step) where it
+    needs fewer flops than the two direct products (4 rows tokens cols), i.e.
+    where cols < 2 tokens; both forms compute the same objective."""
+    if recon == "auto":
+        return "gram" if cols < 2 * tokens else "direct"
+    if recon not in ("direct", "gram"):
+        raise ValueError(f"recon must be 'direct', 'gram' or 'auto', not {recon!r}")
+    return recon
+
+
 def _quantize(W: torch.Tensor, X: torch.Tensor, grid: int, steps: int, lion: GsqLion,
-              tau0: float, tau1: float, init: str, seed: int, stream_id: int):
-    """One layer's annealed solve; returns the hard weights (bf16) and the
-    last relaxed loss."""
-    sol = LayerSolver(W, X, grid, seed=seed, stream_id=stream_id, lion=lion, init=init)
+              tau0: float, tau1: float, init: str, seed: int, stream_id: int, recon: str):
+    """One layer's annealed solve; returns the hard weights (bf16), the last
+    relaxed loss and the reconstruction form used."""
+    form = recon_form(recon, W.shape[1], X.shape[0])
+    sol = LayerSolver(W, X, grid, seed=seed, stream_id=stream_id, lion=lion, init=init,
+                      recon=form)
     losses, (codes, _, s16) = sol.solve(steps, tau0, tau1, log_every=steps)
     Wq = torch.empty_like(W)
     layer = GsqLayer.make(grid, W.shape[0], W.shape[1], DTYPE_BF16)
     gsq_dequant_bf16(layer, codes, s16.view(torch.int16), Wq)
-    return Wq, losses[-1]
+    return Wq, losses[-1], form
 
 
 def staged_quantize(cfg: BlockConfig, w: dict, x: torch.Tensor, grid: int, steps: int,
                     lion: GsqLion | None = None, tau0: float = 1.0, tau1: float = 0.05,
-                    init: str = "rtn", seed: int = 0):
+                    init: str = "rtn", seed: int = 0, recon: str = "direct"):
     """The staged schedule. Returns ``(wq, info)``: the weights with every
     projection replaced by its hard quantized version, and per stage the wall
-    time, the calibration inputs used and the last relaxed loss."""
+    time, the calibration inputs used, the last relaxed loss and each layer's
+    reconstruction form (``recon``: "direct", "gram" or "auto", see
+    :func:`recon_form`)."""
+    recon_form(recon, 1, 1)   # reject an unknown form before any work
     lion = lion or GsqLion.make()
     wq = dict(w)
     info = {}
@@ -143,25 +160,26 @@ def staged_quantize(cfg: BlockConfig, w: dict, x: torch.Tensor, grid: int, steps
     def s1():
         xa = forward(cfg, wq, x)["x_attn"]
         qk = torch.cat([w["q"], w["k"]], dim=0)
-        hq, loss = _quantize(qk, xa, grid, steps, lion, tau0, tau1, init, seed, 0)
+        hq, loss, f = _quantize(qk, xa, grid, steps, lion, tau0, tau1, init, seed, 0, recon)
         wq["q"], wq["k"] = hq[:cfg.q_dim].contiguous(), hq[cfg.q_dim:].contiguous()
-        return {"x": xa, "loss": loss}
+        return {"x": xa, "loss": loss, "recon": {"q_k": f}}
 
     def s2():
         xa = forward(cfg, wq, x)["x_attn"]
-        wq["v"], lv = _quantize(w["v"], xa, grid, steps, lion, tau0, tau1, init, seed, 1)
+        wq["v"], lv, fv = _quantize(w["v"], xa, grid, steps, lion, tau0, tau1, init, seed, 1, recon)
         xo = forward(cfg, wq, x)["x_o"]
-        wq["o"], lo = _quantize(w["o"], xo, grid, steps, lion, tau0, tau1, init, seed, 2)
-        return {"x": xo, "loss": lv + lo}
+        wq["o"], lo, fo = _quantize(w["o"], xo, grid, steps, lion, tau0, tau1, init, seed, 2, recon)
+        return {"x": xo, "loss": lv + lo, "recon": {"v": fv, "o": fo}}
 
     def s3():
         xm = forward(cfg, wq, x)["x_mlp"]
         gu = torch.cat([w["gate"], w["up"]], dim=0)
-        hgu, lgu = _quantize(gu, xm, grid, steps, lion, tau0, tau1, init, seed, 3)
+        hgu, lgu, fgu = _quantize(gu, xm, grid, steps, lion, tau0, tau1, init, seed, 3, recon)
         wq["gate"], wq["up"] = hgu[:cfg.mlp].contiguous(), hgu[cfg.mlp:].contiguous()
         xd = forward(cfg, wq, x)["x_down"]
-        wq["down"], ld = _quantize(w["down"], xd, grid, steps, lion, tau0, tau1, init, seed, 4)
-        return {"x": xd, "loss": lgu + ld}
+        wq["down"], ld, fd = _quantize(w["down"], xd, grid, steps, lion, tau0, tau1, init, seed, 4,
+                                       recon)
+        return {"x": xd, "loss": lgu + ld, "recon": {"gate_up": fgu, "down": fd}}
 
     stage("q_k", s1)
     stage("v_o", s2)

@@ -1,5 +1,6 @@
 """bench.py's output contract: one JSON line with the required keys (GPU),
-and a clear refusal of more than one GPU (CPU)."""
+and a clear refusal of more than one GPU (CPU); the staged schedule's choice
+of reconstruction form (CPU)."""
 
 import json
 import os
@@ -16,6 +17,20 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_block_recon_form_choice():
+    """The staged schedule's "auto" form takes the Gram form exactly where it
+    needs fewer flops (2 rows cols^2 < 4 rows tokens cols)."""
+    pytest.importorskip("torch")
+    from post_weight_quantization_philox_amd.block import recon_form
+    assert recon_form("auto", 4096, 4096) == "gram"       # query/key, value, output, gate/up
+    assert recon_form("auto", 14336, 4096) == "direct"    # down: cols > 2 tokens
+    assert recon_form("auto", 8192, 4096) == "direct"     # equal cost: the direct products
+    assert recon_form("direct", 4096, 4096) == "direct"
+    assert recon_form("gram", 14336, 4096) == "gram"
+    with pytest.raises(ValueError):
+        recon_form("fast", 4096, 4096)
 
 
 @pytest.mark.gpu

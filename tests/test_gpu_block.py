@@ -138,18 +138,21 @@ def test_block_forward_matches_mirror(dev):
         assert e <= 4 * 2.0 ** -8, k
 
 
-def test_staged_schedule(dev):
-    """The staged schedule on a small block: each stage's calibration inputs
-    equal the oracle's mirror forward with the GPU's quantized weights of the
-    earlier stages, every projection ends quantized (dequantised values on the
-    grid), and the quantized block's output error is reported against the
+@pytest.mark.parametrize("recon", ["direct", "gram"])
+def test_staged_schedule(dev, recon):
+    """The staged schedule on a small block, with every layer on the direct
+    products or on the Gram form: each stage's calibration inputs equal the
+    oracle's mirror forward with the GPU's quantized weights of the earlier
+    stages, every projection ends quantized (dequantised values on the grid),
+    and the quantized block's output error is reported against the
     round-to-nearest block."""
     import torch
     import post_weight_quantization_philox_amd as g
     from post_weight_quantization_philox_amd.block import forward, staged_quantize
     cfg, w_np, w_dev, x, xd = _small_block(dev, seed=4)
     wq, info = staged_quantize(cfg, w_dev, xd, oracle.GRID_INT2, 24,
-                               g.GsqLion.make(lr_logit=5e-2, lr_scale=1e-6))
+                               g.GsqLion.make(lr_logit=5e-2, lr_scale=1e-6), recon=recon)
+    assert all(f == recon for v in info.values() for f in v["recon"].values())
     wq_np = dict(w_np)
     for name in ("q", "k", "v", "o", "gate", "up", "down"):
         wq_np[name] = bf16_values(wq[name]).astype(np.float64)
@@ -173,6 +176,6 @@ def test_staged_schedule(dev):
     full = ob.block_forward(x, w_np, SMALL)["out"]
     e_gsq = _nrm(ob.block_forward(x, wq_np, SMALL)["out"], full)
     e_rtn = _nrm(ob.block_forward(x, w_rtn, SMALL)["out"], full)
-    report("staged schedule", x_down_vs_mirror=e_in, x_o_vs_mirror=e_xo, out_err_gsq=e_gsq,
+    report(f"staged schedule ({recon})", x_down_vs_mirror=e_in, x_o_vs_mirror=e_xo, out_err_gsq=e_gsq,
            out_err_rtn=e_rtn, **{f"{k}_s": v["seconds"] for k, v in info.items()})
     assert e_in <= 4 * 2.0 ** -8 and e_xo <= 4 * 2.0 ** -8
