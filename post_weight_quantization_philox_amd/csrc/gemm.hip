@@ -179,7 +179,6 @@ template <int EPI, bool GROUPED, int TBN>
 __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb) {
     static_assert(TBN == 256 || TBN == 128, "tile width 256 or 128");
     static_assert(!GROUPED || TBN == BN, "expert batches use the full tile");
-    static_assert(EPI != EPI_F32_GRAM || TBN == BN, "the Gram form uses the full tile");
     constexpr int WN = TBN / 2;      // wave tile width
     constexpr int NB = WN / 32;      // 32-column MFMA blocks per wave
     constexpr int QB = TBN / 32;     // DMA row groups of the B tile
@@ -391,12 +390,14 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     // Gram form: the dW values a slab pairs with, loaded one slab ahead so
     // their latency overlaps the previous slab's work (zero outside the
     // matrix).
+    // Same lane -> (row, 4 columns) map as the fp32 store below.
     uint2 dv[2][16];
     auto load_dv = [&](int a, uint2 (&d)[16]) {
+        constexpr int LPR = WN / 4;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t = 0; t < 32 * LPR / 64; ++t) {
             const int c = lane + 64 * t;
-            const int grow = grow0 + a * 32 + (c >> 5), gcol = gcol0 + (c & 31) * 4;
+            const int grow = grow0 + a * 32 + c / LPR, gcol = gcol0 + (c % LPR) * 4;
             d[t] = (grow < g.I && gcol < g.J)
                        ? *reinterpret_cast<const uint2*>(g.D + static_cast<int64_t>(grow) * g.ldd + gcol)
                        : make_uint2(0u, 0u);
@@ -592,27 +593,24 @@ hipError_t run_gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t l
         bb > static_cast<int64_t>(kOob) - 2 * static_cast<int64_t>(Rd))
         return hipErrorInvalidValue;
     g.C = C; g.alpha = alpha;
-    // The Gram form keeps full tiles (its products are whole rounds here).
-    const Split sp = EPI == EPI_F32_GRAM ? Split{Split::FULL, 0} : plan_split(I, J);
+    const Split sp = plan_split(I, J);
     const int ti = cdiv(I, BM), tj = cdiv(J, BN);
     float* tail_partials = nullptr;
     switch (sp.kind) {
         case Split::NARROW:
-            if constexpr (EPI != EPI_F32_GRAM) launch_part<EPI, 128>(g, 0, 0, I, J, partials, st);
+            launch_part<EPI, 128>(g, 0, 0, I, J, partials, st);
             break;
         case Split::COLS:
             launch_part<EPI, BN>(g, 0, 0, I, sp.at * BN, partials, st);
             g.fin_loss = nullptr;
             if (partials) tail_partials = partials + ti * sp.at;
-            if constexpr (EPI != EPI_F32_GRAM)
-                launch_part<EPI, 128>(g, 0, sp.at * BN, I, J - sp.at * BN, tail_partials, st);
+            launch_part<EPI, 128>(g, 0, sp.at * BN, I, J - sp.at * BN, tail_partials, st);
             break;
         case Split::ROWS:
             launch_part<EPI, BN>(g, 0, 0, sp.at * BM, J, partials, st);
             g.fin_loss = nullptr;
             if (partials) tail_partials = partials + sp.at * tj;
-            if constexpr (EPI != EPI_F32_GRAM)
-                launch_part<EPI, 128>(g, sp.at * BM, 0, I - sp.at * BM, J, tail_partials, st);
+            launch_part<EPI, 128>(g, sp.at * BM, 0, I - sp.at * BM, J, tail_partials, st);
             break;
         default:
             launch_part<EPI, BN>(g, 0, 0, I, J, partials, st);
@@ -743,7 +741,7 @@ hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t r
 }
 
 size_t gram_partials(int64_t rows, int64_t cols) {
-    return static_cast<size_t>(cdiv(rows, BM)) * cdiv(cols, BN);
+    return static_cast<size_t>(product_workgroups(static_cast<int>(rows), static_cast<int>(cols)));
 }
 
 hipError_t launch_gram(int64_t tokens, int64_t cols, const uint16_t* XT, uint16_t* H,

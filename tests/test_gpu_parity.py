@@ -295,6 +295,7 @@ def test_recon_loss_grad(dev, M, N, K, offs):
     (512, 256, 512),                  # several tiles
     (300, 192, 384),                  # ragged rows, partial tiles
     (256, 64, 640),                   # few tokens, in-features past two tiles
+    (4352, 64, 4096),                 # 17x16 tiles: a row block of whole rounds + a 128-wide tail
 ])
 def test_recon_gram(dev, M, N, K):
     import torch
