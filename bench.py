@@ -347,12 +347,13 @@ def main():
     loss = float(solver.loss.item())
     ms_per_step = elapsed * 1e3 / args.steps
 
-    # Dominant single kernel: the recon call is two GEMM launches of equal
-    # flops, so each GEMM launch is weighed at its share of the call.
+    # Dominant single kernel: the recon call is two products of equal flops
+    # (each one launch, or two when its last round is split into 256x128
+    # tiles), so each product is weighed at its share of the call.
     dominant = max(per_launch, key=per_launch.get)
     if dominant == "recon_loss_grad":
         ach = kernels[dominant]["TFLOP/s"]
-        roof = {"bound": "mfma", "kernel": "gemm_nt_kernel (both launches of the call)",
+        roof = {"bound": "mfma", "kernel": "gemm_nt_kernel (both products of the call)",
                 "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
     else:
