@@ -53,6 +53,28 @@ def test_matmul_nt(dev, I, J, R):
     assert np.all(np.abs(bf16_values(C) - ref) <= 0.5 * bf16_ulp(ref) + gam + 1e-30)
 
 
+def test_matmul_nt_strided_split(dev):
+    """Padded leading dimensions on a product split into a row block of whole
+    rounds and a 128-wide tail: the tail's operand and output offsets follow
+    lda, ldb and ldc, and the padding is neither read into the result nor
+    written."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    rng = np.random.default_rng(11)
+    I, J, R, lda, ldb, ldc = 5000, 4000, 64, 72, 80, 4008
+    a_bits, A = _rand_bf16(rng, (I, lda))
+    b_bits, B = _rand_bf16(rng, (J, ldb))
+    C = torch.full((I, ldc), -1.0, dtype=torch.bfloat16, device=dev)
+    g.gsq_matmul_nt_bf16(I, J, R, to_dev_bf16(a_bits, dev), lda, to_dev_bf16(b_bits, dev), ldb, C,
+                         ldc)
+    torch.cuda.synchronize()
+    got = bf16_values(C)
+    ref = A[:, :R] @ B[:, :R].T
+    gam = (R + 2) * 2.0 ** -24 * (np.abs(A[:, :R]) @ np.abs(B[:, :R]).T)
+    assert np.all(np.abs(got[:, :J] - ref) <= 0.5 * bf16_ulp(ref) + gam + 1e-30)
+    assert np.all(got[:, J:] == -1.0)
+
+
 def test_rmsnorm_softmax_silu_add(dev):
     import torch
     import post_weight_quantization_philox_amd as g
