@@ -111,6 +111,50 @@ def test_recon_validation(L):
     assert g.gsq_recon_workspace_bytes(1, offs_bad, 64, 256) == 0
 
 
+def _tiles(n, t):
+    return -(-n // t)
+
+
+def _product_workgroups(I, J):
+    """Workgroups of one I x J product (one loss partial each): whole rounds
+    of 256 full 256x256 tiles on a column block or a row block, the rest in
+    256x128 tiles; under half a round, 256x128 tiles throughout."""
+    ti, tj = _tiles(I, 256), _tiles(J, 256)
+    T = ti * tj
+    if T % 256 == 0:
+        return T
+    if 2 * T <= 256:
+        return ti * _tiles(J, 128)
+    n0 = 256 // np.gcd(ti, 256)
+    jm = tj // n0 * n0
+    if 0 < jm < tj and ti * (tj - jm) * 2 <= 256:
+        return ti * jm + ti * _tiles(J - 256 * jm, 128)
+    m0 = 256 // np.gcd(tj, 256)
+    im = ti // m0 * m0
+    if 0 < im < ti and (ti - im) * tj * 2 <= 256:
+        return im * tj + (ti - im) * _tiles(J, 128)
+    return T
+
+
+@pytest.mark.parametrize("rows,tokens,want", [
+    (4096, 4096, 256),          # one whole round of full tiles
+    (1024, 4096, 4 * 32),       # under half a round: 128-wide tiles
+    (5000, 4096, 16 * 16 + 4 * 32),    # a row block of whole rounds + tail
+    (4000, 5056, 16 * 16 + 16 * 8),    # a column block of whole rounds + ragged tail
+    (28672, 8192, 112 * 32),    # 14 whole rounds
+    (300, 192, 2 * 2),          # partial tiles, 128 wide
+])
+def test_workspace_follows_the_launch_plan(L, rows, tokens, want):
+    """The recon and Gram workspaces hold one fp32 loss partial per workgroup
+    of the product that writes them, as the launch plan splits it."""
+    assert _product_workgroups(rows, tokens) == want
+    size = lambda n: (n * 4 + 255) // 256 * 256 + 256
+    assert g.gsq_recon_workspace_bytes(1, [0, tokens], rows, 256) == size(want)
+    # The Gram form's product is rows x cols (cols a multiple of 128).
+    if tokens % 128 == 0:
+        assert g.gsq_recon_gram_workspace_bytes(rows, tokens) == size(want)
+
+
 def test_gram_validation(L):
     gr = g.lib().gsq_gram
     assert gr(100, 256, FAKE, FAKE, None) == ERR_SHAPE                 # tokens not a multiple of 64
