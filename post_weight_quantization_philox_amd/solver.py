@@ -211,15 +211,36 @@ class LayerSolver:
         gsq_harden_pack(self.layer, self.logits, self.scales, self.init_codes, codes, packed, s16)
         return codes, packed, s16
 
+    STATE = ("logits", "mom", "scales", "scale_mom", "codes")
+
+    def state(self) -> dict:
+        """Device copies of everything a solve carries from step to step:
+        logits, Lion momenta, scales, scale momenta and the warm-start codes
+        (local shift's centres). With the step index it is a checkpoint: the
+        noise is a function of (seed, stream id, step, coordinate), so no
+        generator state is needed and a resumed solve replays bit for bit."""
+        return {k: getattr(self, k).clone() for k in self.STATE}
+
+    def load_state(self, state: dict):
+        """Restore a :meth:`state` taken from a solver of the same layer."""
+        for k in self.STATE:
+            getattr(self, k).copy_(state[k])
+
     def solve(self, steps: int, tau0: float = 1.0, tau1: float = 0.05, noise_scale: float = 1.0,
-              log_every: int = 0):
-        """The annealed solve; returns the per-step losses (host, every step
-        if ``log_every`` is 1, else only those logged) and the hard result."""
+              log_every: int = 0, start: int = 0, stop: int | None = None):
+        """The annealed solve over the schedule of ``steps`` temperatures,
+        running steps ``start`` .. ``stop - 1`` (default: all). Returns the
+        per-step losses (host, every step if ``log_every`` is 1, else only
+        those logged) and the hard result, or None for it when the solve
+        stops early (take :meth:`state` to resume it with ``start=stop``)."""
         losses = []
         taus = tau_schedule(steps, tau0, tau1)
-        self.relax_fwd(0, taus[0], noise_scale)
-        for t, tau in enumerate(taus):
-            self.step_fused(t, tau, taus[t + 1] if t + 1 < steps else None, noise_scale)
+        stop = steps if stop is None else stop
+        if not 0 <= start < stop <= steps:
+            raise ValueError("need 0 <= start < stop <= steps")
+        self.relax_fwd(start, taus[start], noise_scale)
+        for t in range(start, stop):
+            self.step_fused(t, taus[t], taus[t + 1] if t + 1 < stop else None, noise_scale)
             if log_every and (t % log_every == 0 or t == steps - 1):
                 losses.append(float(self.loss.item()))
-        return losses, self.harden()
+        return losses, (self.harden() if stop == steps else None)

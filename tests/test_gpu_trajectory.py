@@ -235,3 +235,37 @@ def test_expert_batch_trajectory_matches_oracle():
     assert agree >= 0.999
     assert moved > 0.001
     assert idle == 0.0                # no tokens: zero gradient, Lion leaves the logits alone
+
+
+@pytest.mark.parametrize("grid", [oracle.GRID_INT2, oracle.GRID_INT3_LOCAL])
+def test_resume_from_checkpoint_is_bit_identical(grid):
+    """A solve stopped after step 9, checkpointed (logits, momenta, scales,
+    scale momenta, warm-start codes) and resumed at step 10 in a fresh solver
+    of the same layer ends in exactly the state and hard codes of the
+    uninterrupted solve: the noise needs no saved generator state."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver
+    dev = device()
+    d = synthetic.small_layer(256, 512, 128, seed=3, w_bf16=True)
+    W, X = to_dev_bf16(d["W_bits"], dev), to_dev_bf16(d["X_bits"], dev)
+    make = lambda: LayerSolver(W, X, grid, seed=7, stream_id=2,
+                               lion=g.GsqLion.make(lr_logit=5e-2, lr_scale=1e-5))
+    T = 20
+    whole = make()
+    l_whole, (codes_w, packed_w, s16_w) = whole.solve(T, 1.0, 0.1, log_every=1)
+    first = make()
+    l_first, hard = first.solve(T, 1.0, 0.1, log_every=1, stop=10)
+    assert hard is None
+    ckpt = first.state()
+    del first
+    resumed = make()
+    resumed.load_state(ckpt)
+    l_rest, (codes_r, packed_r, s16_r) = resumed.solve(T, 1.0, 0.1, log_every=1, start=10)
+    assert l_first + l_rest == l_whole
+    for k in ("logits", "mom", "scales", "scale_mom"):
+        assert torch.equal(getattr(whole, k), getattr(resumed, k)), k
+    assert torch.equal(codes_w, codes_r) and torch.equal(packed_w, packed_r)
+    assert torch.equal(s16_w.view(torch.int16), s16_r.view(torch.int16))
+    with pytest.raises(ValueError):
+        resumed.solve(T, 1.0, 0.1, start=T)
