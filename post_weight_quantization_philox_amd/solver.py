@@ -18,6 +18,8 @@ Memory per coordinate: 8L bytes of logits + momentum, 1 (codes), 2 (dW),
 
 from __future__ import annotations
 
+import json
+
 import math
 
 import numpy as np
@@ -227,12 +229,23 @@ class LayerSolver:
             getattr(self, k).copy_(state[k])
 
     def solve(self, steps: int, tau0: float = 1.0, tau1: float = 0.05, noise_scale: float = 1.0,
-              log_every: int = 0, start: int = 0, stop: int | None = None):
+              log_every: int = 0, start: int = 0, stop: int | None = None,
+              log_path: str | None = None):
         """The annealed solve over the schedule of ``steps`` temperatures,
         running steps ``start`` .. ``stop - 1`` (default: all). Returns the
         per-step losses (host, every step if ``log_every`` is 1, else only
         those logged) and the hard result, or None for it when the solve
-        stops early (take :meth:`state` to resume it with ``start=stop``)."""
+        stops early (take :meth:`state` to resume it with ``start=stop``).
+        With ``log_path`` every logged step is also appended there as one
+        JSON line: step, tau, loss, layer shape, grid, seed and stream id."""
+        log = open(log_path, "a") if log_path and log_every else None
+        try:
+            return self._solve(steps, tau0, tau1, noise_scale, log_every, start, stop, log)
+        finally:
+            if log is not None:
+                log.close()
+
+    def _solve(self, steps, tau0, tau1, noise_scale, log_every, start, stop, log):
         losses = []
         taus = tau_schedule(steps, tau0, tau1)
         stop = steps if stop is None else stop
@@ -243,4 +256,9 @@ class LayerSolver:
             self.step_fused(t, taus[t], taus[t + 1] if t + 1 < stop else None, noise_scale)
             if log_every and (t % log_every == 0 or t == steps - 1):
                 losses.append(float(self.loss.item()))
+                if log is not None:
+                    log.write(json.dumps({"step": t, "tau": taus[t], "loss": losses[-1],
+                                          "rows": self.rows, "cols": self.cols,
+                                          "grid": self.grid, "seed": self.layer.seed,
+                                          "stream": self.layer.stream}) + "\n")
         return losses, (self.harden() if stop == steps else None)

@@ -238,7 +238,7 @@ def test_expert_batch_trajectory_matches_oracle():
 
 
 @pytest.mark.parametrize("grid", [oracle.GRID_INT2, oracle.GRID_INT3_LOCAL])
-def test_resume_from_checkpoint_is_bit_identical(grid):
+def test_resume_from_checkpoint_is_bit_identical(grid, tmp_path):
     """A solve stopped after step 9, checkpointed (logits, momenta, scales,
     scale momenta, warm-start codes) and resumed at step 10 in a fresh solver
     of the same layer ends in exactly the state and hard codes of the
@@ -253,7 +253,13 @@ def test_resume_from_checkpoint_is_bit_identical(grid):
                                lion=g.GsqLion.make(lr_logit=5e-2, lr_scale=1e-5))
     T = 20
     whole = make()
-    l_whole, (codes_w, packed_w, s16_w) = whole.solve(T, 1.0, 0.1, log_every=1)
+    log = tmp_path / "solve.jsonl"
+    l_whole, (codes_w, packed_w, s16_w) = whole.solve(T, 1.0, 0.1, log_every=1, log_path=str(log))
+    import json
+    rows = [json.loads(line) for line in log.read_text().splitlines()]
+    assert [r["step"] for r in rows] == list(range(T))
+    assert [r["loss"] for r in rows] == l_whole
+    assert rows[0]["seed"] == 7 and rows[0]["stream"] == 2 and rows[0]["grid"] == grid
     first = make()
     l_first, hard = first.solve(T, 1.0, 0.1, log_every=1, stop=10)
     assert hard is None
