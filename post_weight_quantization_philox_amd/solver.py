@@ -237,7 +237,8 @@ class LayerSolver:
         those logged) and the hard result, or None for it when the solve
         stops early (take :meth:`state` to resume it with ``start=stop``).
         With ``log_path`` every logged step is also appended there as one
-        JSON line: step, tau, loss, layer shape, grid, seed and stream id."""
+        JSON line: step, tau, loss, layer shape, grid, seed and stream id. A
+        logged loss that is not finite raises FloatingPointError."""
         log = open(log_path, "a") if log_path and log_every else None
         try:
             return self._solve(steps, tau0, tau1, noise_scale, log_every, start, stop, log)
@@ -256,6 +257,10 @@ class LayerSolver:
             self.step_fused(t, taus[t], taus[t + 1] if t + 1 < stop else None, noise_scale)
             if log_every and (t % log_every == 0 or t == steps - 1):
                 losses.append(float(self.loss.item()))
+                if not math.isfinite(losses[-1]):
+                    # A non-finite input (weights, activations or state) has
+                    # reached the objective: stop instead of optimising NaNs.
+                    raise FloatingPointError(f"non-finite loss {losses[-1]} at step {t}")
                 if log is not None:
                     log.write(json.dumps({"step": t, "tau": taus[t], "loss": losses[-1],
                                           "rows": self.rows, "cols": self.cols,

@@ -275,3 +275,21 @@ def test_resume_from_checkpoint_is_bit_identical(grid, tmp_path):
     assert torch.equal(s16_w.view(torch.int16), s16_r.view(torch.int16))
     with pytest.raises(ValueError):
         resumed.solve(T, 1.0, 0.1, start=T)
+
+
+def test_non_finite_input_stops_the_solve():
+    """A NaN among the calibration activations reaches the objective in the
+    first step; the solve raises instead of optimising NaNs. (Activations
+    enter only arithmetic, never an index, so a NaN cannot misdirect a memory
+    access.)"""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver
+    dev = device()
+    d = synthetic.small_layer(256, 256, 64, seed=5, w_bf16=True)
+    x_bits = d["X_bits"].copy()
+    x_bits[3, 17] = 0x7FC0                  # bf16 quiet NaN
+    sol = LayerSolver(to_dev_bf16(d["W_bits"], dev), to_dev_bf16(x_bits, dev), g.GRID_INT2,
+                      seed=0, stream_id=0)
+    with pytest.raises(FloatingPointError, match="step 0"):
+        sol.solve(4, 1.0, 0.1, log_every=1)
