@@ -163,8 +163,13 @@ def time_fused(solver, taus, warmup: int, steps: int, stream):
     pass) + backward and Lion of step t fused with the forward of step t + 1."""
     import numpy as np
     import torch
+    # The spin-up steps change the state; the timed steps start from the
+    # warm start again, so every run times the same trajectory.
+    start = solver.state()
     solver.relax_fwd(0, taus[0])
     spin_up(lambda: solver.step_fused(0, taus[0], taus[1]))
+    solver.load_state(start)
+    del start
     solver.relax_fwd(0, taus[0])
     for t in range(warmup):
         solver.step_fused(t, taus[t], taus[t + 1])

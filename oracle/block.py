@@ -1,5 +1,6 @@
-"""Plain CPU oracle of a synthetic transformer block and of GSQ's staged
-schedule over it (NumPy, fp64).
+"""Plain CPU oracle of a synthetic transformer block (NumPy, fp64): the
+forward pass whose intermediate activations are the calibration inputs of
+GSQ's staged block schedule.
 
 TEST INFRASTRUCTURE. Only ``tests/`` may import this module. It shares no
 code with the GPU library and the GPU library never calls it.
@@ -8,10 +9,14 @@ The pages optimise a decoder block in stages: the query and key projections
 first, then value and output projections, then the MLP on the block's
 output, each stage frozen before the next and its quantized outputs
 propagated to the next stage's inputs (agihunt.info, optimizer paragraph on
-the staged block schedule). The block here is a Llama-shaped decoder block
-with random weights: RMSNorm, causal multi-head attention with grouped key /
-value heads (no positional rotation: the schedule, not the model, is the
-subject), a residual, RMSNorm, a SwiGLU MLP and a residual.
+the staged block schedule). The schedule itself is host sequencing and is
+not repeated here; this module holds the block it runs over, so that the
+inputs every stage sees can be checked. The block is a Llama-shaped decoder
+block with random weights: RMSNorm, causal multi-head attention with grouped
+key / value heads (no positional rotation: the schedule, not the model, is
+the subject), a residual, RMSNorm, a SwiGLU MLP and a residual.
+:func:`block_forward` is exact fp64; :func:`block_forward_mirror` is the same
+forward with bfloat16 roundings where the GPU stores an intermediate.
 """
 
 from __future__ import annotations
@@ -64,7 +69,8 @@ def attention(xn, Wq, Wk, Wv, heads: int, kv_heads: int, head_dim: int):
 
 def block_forward(x, w: dict, cfg: dict):
     """The block's output and the inputs each projection sees:
-    ``{"out", "x_attn", "x_o", "x_mlp", "x_down"}``."""
+    ``{"out", "x_attn", "x_o", "h", "x_mlp", "x_down"}`` (``h`` is the
+    residual stream after attention)."""
     x = np.asarray(x, dtype=np.float64)
     xa = rmsnorm(x, w["g_attn"])
     ao = attention(xa, w["q"], w["k"], w["v"], cfg["heads"], cfg["kv_heads"], cfg["head_dim"])
@@ -73,7 +79,7 @@ def block_forward(x, w: dict, cfg: dict):
     act = silu_mul(xm @ np.asarray(w["gate"], dtype=np.float64).T,
                    xm @ np.asarray(w["up"], dtype=np.float64).T)
     out = h + act @ np.asarray(w["down"], dtype=np.float64).T
-    return {"out": out, "x_attn": xa, "x_o": ao, "x_mlp": xm, "x_down": act}
+    return {"out": out, "x_attn": xa, "x_o": ao, "h": h, "x_mlp": xm, "x_down": act}
 
 
 def dequantize(codes, scales_f16_bits, grid: int, group: int = 128):

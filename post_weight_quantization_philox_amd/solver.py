@@ -126,6 +126,13 @@ class LayerSolver:
             gsq_init_gptq(self.layer, self.W, self.tokens, self.XT, damp, init_logit, ws,
                           self.scales, self.codes, self.logits, self.gptq_info)
             del ws
+            info = int(self.gptq_info.item())
+            if info != 0:
+                # A non-positive pivot: the factor (and so the warm start) is
+                # meaningless; more damping is the usual remedy.
+                raise FloatingPointError(
+                    f"GPTQ warm start: the damped Gram matrix X^T X + damp I is not positive "
+                    f"definite at reversed column {info - 1} (damp={damp})")
         else:
             gsq_init_rtn(self.layer, self.W, self.scales, self.codes, self.logits, init_logit)
         if recon == "gram":

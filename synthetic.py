@@ -64,11 +64,23 @@ WORKLOADS = {
 }
 
 
+_CHUNK = 1 << 24
+
+
 def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """fp32 array -> bfloat16 bit patterns (uint16), nearest even."""
+    """fp32 array -> bfloat16 bit patterns (uint16), nearest even.
+
+    Works in 32-bit words, in chunks: where b + 0x7FFF + lsb wraps past 2^32
+    (only NaN patterns), the kept bits (sum >> 16) mod 2^16 are the same as
+    with a wider sum."""
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = (b.astype(np.uint64) + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    out = np.empty(b.shape, dtype=np.uint16)
+    fb, fo = b.reshape(-1), out.reshape(-1)
+    for i in range(0, fb.size, _CHUNK):
+        c = fb[i:i + _CHUNK]
+        fo[i:i + _CHUNK] = (c + np.uint32(0x7FFF) + ((c >> np.uint32(16)) & np.uint32(1))) \
+            >> np.uint32(16)
+    return out
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:

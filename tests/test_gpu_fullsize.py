@@ -302,53 +302,33 @@ def test_beyond_32bit_offsets():
     _log("beyond 2^30: fused backward + Lion + next forward ok")
 
 
-# Warm-start logit and logit learning rate chosen so that hard codes move
-# within the steps: a ternary code changes only when a logit crosses 0, so
-# the ternary layer starts nearer to it.
-@pytest.mark.parametrize("name,init_logit,lr_logit", [("qproj4096_int2", 2.0, 5e-2),
-                                                      ("downproj4096x14336_ternary", 0.5, 5e-2),
-                                                      ("gateproj28672x8192_int3local", 2.0, 5e-2)])
-def test_fullsize_trajectory_sampled_rows(name, init_logit, lr_logit):
-    """An annealed solve of the whole layer in the launch configuration the
-    bench times (objective, then fused backward + Lion + next forward)
-    against the oracle's step loop on sampled rows. Rows are independent in
-    the objective (R[:, r] = X dW[r]^T, G[r] = 2 R[:, r]^T X) and each row's
-    noise counters follow its place in the layer, so the oracle runs every
-    sampled row on its own. Compared: every step teacher-forced (the oracle's
-    step from the GPU's state before it against the GPU's state after it),
-    and the free-running curves: the sampled rows' loss at every step (the
-    GPU's from its bf16 R^T) and the final hard codes."""
-    import torch
-    import post_weight_quantization_philox_amd as g
-    from post_weight_quantization_philox_amd.solver import LayerSolver, tau_schedule
-    dev = device()
-    t0 = time.time()
-    d = synthetic.generate(name, seed=0)
+def _trajectory_rows(sol, d, rows, x_of_row, gpu_row_loss, T, lr_logit, lr_scale, sid,
+                     init_logit, label, t0):
+    """Run ``T`` annealed steps of ``sol`` (objective, then fused backward +
+    Lion + next forward, at the solver's own temperatures) and compare the
+    sampled ``rows`` with the oracle's step loop at the oracle's temperatures,
+    teacher-forced and free-running. ``x_of_row(r)`` is the calibration block
+    row r sees; ``gpu_row_loss()`` reads the sampled rows' losses from the
+    GPU's bf16 R^T after a step."""
+    from post_weight_quantization_philox_amd.solver import tau_schedule
     grid = d["workload"].grid
-    T, lr_scale, sid = 24, 1e-5, 3
-    taus = tau_schedule(T, 1.0, 0.05)
-    sol = LayerSolver(to_dev_bf16(d["W_bits"], dev), to_dev_bf16(d["X_bits"], dev), grid, seed=0,
-                      stream_id=sid, lion=g.GsqLion.make(lr_logit=lr_logit, lr_scale=lr_scale),
-                      init_logit=init_logit)
-    M, K, N = sol.rows, sol.cols, sol.tokens
-    rows = _sample_rows(M, M)
-    RT = sol.RT.view(M, N)
+    gpu_taus = tau_schedule(T, 1.0, 0.05)
+    taus = oracle.tau_schedule(T, 1.0, 0.05)
+
     def snap():
         return (f32(sol.logits[:, rows]), f32(sol.mom[:, rows]), f32(sol.scales[rows]),
                 f32(sol.scale_mom[rows]))
 
-    sol.relax_fwd(0, taus[0])
+    sol.relax_fwd(0, gpu_taus[0])
     gpu = np.zeros((T, len(rows)))
     states = [snap()]
     for t in range(T):
-        sol.step_fused(t, taus[t], taus[t + 1] if t + 1 < T else None)
-        rt = bf16_values(RT[rows]).astype(np.float64)
-        gpu[t] = (rt * rt).sum(axis=1)
+        sol.step_fused(t, gpu_taus[t], gpu_taus[t + 1] if t + 1 < T else None)
+        gpu[t] = gpu_row_loss()
         states.append(snap())
     codes = sol.harden()[0][rows].cpu().numpy()
-    _log(f"{name}: {T} GPU steps done; oracle on rows {rows}")
+    _log(f"{label}: {T} GPU steps done; oracle on rows {rows}")
     W = d["W"]
-    X = d["X"].astype(np.float64)
     s, c0, lg = oracle.init_rtn(W[rows], grid, init_logit=init_logit)
     ref = np.zeros_like(gpu)
     c_ref = np.zeros_like(codes)
@@ -358,8 +338,8 @@ def test_fullsize_trajectory_sampled_rows(name, init_logit, lr_logit):
               "scales": s[j:j + 1].copy(), "scale_mom": np.zeros_like(s[j:j + 1]),
               "codes": c0[j:j + 1]}
         for t in range(T):
-            ref[t, j] = oracle.step(st, W[r:r + 1], X, grid, t, taus[t], 0, sid, lr_logit,
-                                    lr_scale, bf16_dW=True, bf16_RT=True, row0=r)
+            ref[t, j] = oracle.step(st, W[r:r + 1], x_of_row(r), grid, t, float(taus[t]), 0, sid,
+                                    lr_logit, lr_scale, bf16_dW=True, bf16_RT=True, row0=r)
         c_ref[j] = oracle.harden(st["logits"], grid, c0[j:j + 1])[0]
         rows_state.append(st["logits"][:, 0])
     # Teacher-forced: the oracle's step t from the GPU's own state before it,
@@ -373,8 +353,8 @@ def test_fullsize_trajectory_sampled_rows(name, init_logit, lr_logit):
             st = {"logits": lg0[:, j:j + 1].copy(), "mom": m0[:, j:j + 1].copy(),
                   "scales": s0[j:j + 1].copy(), "scale_mom": sm0[j:j + 1].copy(),
                   "codes": c0[j:j + 1]}
-            oracle.step(st, W[r:r + 1], X, grid, t, taus[t], 0, sid, lr_logit, lr_scale,
-                        bf16_dW=True, bf16_RT=True, row0=r)
+            oracle.step(st, W[r:r + 1], x_of_row(r), grid, t, float(taus[t]), 0, sid, lr_logit,
+                        lr_scale, bf16_dW=True, bf16_RT=True, row0=r)
             flips[t] += np.count_nonzero(st["logits"][:, 0] != lg1[:, j])
             sflips[t] += np.count_nonzero(st["scales"][0] != s1[j])
             same = st["logits"][:, 0] == lg1[:, j]
@@ -395,7 +375,7 @@ def test_fullsize_trajectory_sampled_rows(name, init_logit, lr_logit):
     same_logits = float(np.mean(f32(sol.logits[:, rows]) == np.stack(rows_state, axis=1)))
     agree = float(np.mean(codes == c_ref))
     moved = float(np.mean(c_ref != c0))
-    report(f"{name} trajectory on sampled rows", max_rel_loss=float(rel.max()),
+    report(f"{label} trajectory on sampled rows", max_rel_loss=float(rel.max()),
            max_rel_single_row=float(rel_rows.max()), logits_identical=same_logits,
            code_agreement=agree, codes_moved_from_init=moved, max_logit_flips=float(flips.max()),
            max_scale_flips=float(sflips.max()), mom_err=mom_err, seconds=time.time() - t0)
@@ -409,3 +389,88 @@ def test_fullsize_trajectory_sampled_rows(name, init_logit, lr_logit):
     # a code changes.
     assert agree >= 0.995
     assert moved > 0.001
+
+
+# Warm-start logit and logit learning rate chosen so that hard codes move
+# within the steps: a ternary code changes only when a logit crosses 0, so
+# the ternary layer starts nearer to it.
+@pytest.mark.parametrize("name,init_logit,lr_logit", [("qproj4096_int2", 2.0, 5e-2),
+                                                      ("downproj4096x14336_ternary", 0.5, 5e-2),
+                                                      ("gateproj28672x8192_int3local", 2.0, 5e-2)])
+def test_fullsize_trajectory_sampled_rows(name, init_logit, lr_logit):
+    """An annealed solve of the whole layer in the launch configuration the
+    bench times (objective, then fused backward + Lion + next forward)
+    against the oracle's step loop on sampled rows. Rows are independent in
+    the objective (R[:, r] = X dW[r]^T, G[r] = 2 R[:, r]^T X) and each row's
+    noise counters follow its place in the layer, so the oracle runs every
+    sampled row on its own. Compared: every step teacher-forced (the oracle's
+    step from the GPU's state before it against the GPU's state after it),
+    and the free-running curves: the sampled rows' loss at every step (the
+    GPU's from its bf16 R^T) and the final hard codes."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver
+    dev = device()
+    t0 = time.time()
+    d = synthetic.generate(name, seed=0)
+    grid = d["workload"].grid
+    T, lr_scale, sid = 24, 1e-5, 3
+    sol = LayerSolver(to_dev_bf16(d["W_bits"], dev), to_dev_bf16(d["X_bits"], dev), grid, seed=0,
+                      stream_id=sid, lion=g.GsqLion.make(lr_logit=lr_logit, lr_scale=lr_scale),
+                      init_logit=init_logit)
+    M, N = sol.rows, sol.tokens
+    rows = _sample_rows(M, M)
+    RT = sol.RT.view(M, N)
+    X = d["X"].astype(np.float64)
+
+    def gpu_row_loss():
+        rt = bf16_values(RT[rows]).astype(np.float64)
+        return (rt * rt).sum(axis=1)
+
+    _trajectory_rows(sol, d, rows, lambda r: X, gpu_row_loss, T, lr_logit, lr_scale, sid,
+                     init_logit, name, t0)
+
+
+def test_fullsize_expert_batch_trajectory_sampled_rows():
+    """The same annealed comparison on the 64-expert batch (64 x 2048x7168,
+    2-bit, routed token counts Zipf(1.1) on [64, 1024]) in the launch
+    configuration the bench times (grouped products, fused pass over all
+    experts), on sampled rows of the first expert, the last expert and the
+    expert with the most tokens. A row of expert e sees only e's tokens."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver
+    dev = device()
+    t0 = time.time()
+    name = "moe64x2048x7168_int2"
+    d = synthetic.generate(name, seed=0)
+    wl = d["workload"]
+    E, rpe = wl.experts, wl.rows_per_expert
+    T, lr_logit, lr_scale, sid = 24, 5e-2, 1e-5, 3
+    offs = [int(o) for o in d["tok_offsets"]]
+    counts = np.diff(offs)
+    experts = sorted({0, E - 1, int(np.argmax(counts))})
+    _log(f"{name}: inputs drawn in {time.time() - t0:.1f} s; experts {experts} with "
+         f"{[int(counts[e]) for e in experts]} tokens")
+    sol = LayerSolver(to_dev_bf16(d["W_bits"], dev), to_dev_bf16(d["X_bits"], dev), wl.grid,
+                      tok_offsets=offs, rows_per_expert=rpe, seed=0, stream_id=sid,
+                      lion=g.GsqLion.make(lr_logit=lr_logit, lr_scale=lr_scale))
+    poffs = [int(o) for o in sol.tok_offsets]          # padded to 64 on the device
+    rng = np.random.default_rng(1)
+    rows = sorted({e * rpe + int(i) for e in experts
+                   for i in [0, 1, rpe // 2, rpe - 1, *rng.integers(0, rpe, 2)]})
+    X = d["X"].astype(np.float64)
+    x_blocks = {e: X[offs[e]:offs[e + 1]] for e in experts}
+
+    def gpu_row_loss():
+        out = np.zeros(len(rows))
+        for j, r in enumerate(rows):
+            e, i = divmod(r, rpe)
+            n = poffs[e + 1] - poffs[e]
+            blk = sol.RT[rpe * poffs[e]: rpe * poffs[e + 1]].view(rpe, n)
+            rt = bf16_values(blk[i]).astype(np.float64)
+            out[j] = float((rt * rt).sum())
+        return out
+
+    _trajectory_rows(sol, d, rows, lambda r: x_blocks[r // rpe], gpu_row_loss, T, lr_logit,
+                     lr_scale, sid, 2.0, name, t0)

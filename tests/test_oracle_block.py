@@ -83,3 +83,60 @@ def test_dequantize_levels():
     tc = np.array(([0, 1, 2] * 43)[:128], dtype=np.uint8).reshape(1, 128)
     t = ob.dequantize(tc, s16[:1], oracle.GRID_TERNARY)
     np.testing.assert_array_equal(t[0, :3], [-0.5, 0.0, 0.5])
+
+
+def _block_case(seed, n=24, d=32, heads=4, kv_heads=2, hd=8, m=48, bf16=True):
+    """A small block with grouped heads (2 query heads per key/value head),
+    non-unit norm gains and, optionally, bf16-valued weights and tokens."""
+    rng = np.random.default_rng(seed)
+    cfg = {"heads": heads, "kv_heads": kv_heads, "head_dim": hd}
+    shp = {"q": (heads * hd, d), "k": (kv_heads * hd, d), "v": (kv_heads * hd, d),
+           "o": (d, heads * hd), "gate": (m, d), "up": (m, d), "down": (d, m)}
+    rb = (lambda a: oracle.round_bf16(a.astype(np.float32)).astype(np.float64)) if bf16 else (lambda a: a)
+    w = {k: rb(rng.normal(0, 1 / np.sqrt(s[1]), size=s)) for k, s in shp.items()}
+    w["g_attn"] = rng.uniform(0.8, 1.2, d)
+    w["g_mlp"] = rng.uniform(0.8, 1.2, d)
+    return cfg, w, rb(rng.normal(size=(n, d)))
+
+
+KEYS = ("x_attn", "x_o", "h", "x_mlp", "x_down", "out")
+
+
+def test_mirror_without_rounding_is_the_forward(monkeypatch):
+    """With its bfloat16 roundings switched off, the mirror forward is the
+    exact forward: the same heads read the same key/value group, the same
+    causal mask, norms, SwiGLU and residuals (a slip in any of them in the
+    mirror's own inline attention shows here at fp64 precision)."""
+    cfg, w, x = _block_case(5, bf16=False)
+    ref = ob.block_forward(x, w, cfg)
+    monkeypatch.setattr(ob, "_rb", lambda a: np.asarray(a, dtype=np.float64))
+    got = ob.block_forward_mirror(x, w, cfg)
+    for k in KEYS:
+        np.testing.assert_allclose(got[k], ref[k], rtol=1e-12, atol=1e-12, err_msg=k)
+
+
+def test_mirror_head_outputs_equal_attention(monkeypatch):
+    """Each head of the mirror's attention output equals the pinned
+    :func:`attention` of that head alone (rounding off)."""
+    cfg, w, x = _block_case(6, bf16=False)
+    monkeypatch.setattr(ob, "_rb", lambda a: np.asarray(a, dtype=np.float64))
+    ao = ob.block_forward_mirror(x, w, cfg)["x_o"]
+    xa = ob.rmsnorm(x, w["g_attn"])
+    hd, group = cfg["head_dim"], cfg["heads"] // cfg["kv_heads"]
+    for h in range(cfg["heads"]):
+        g = h // group
+        one = ob.attention(xa, w["q"][h * hd:(h + 1) * hd], w["k"][g * hd:(g + 1) * hd],
+                           w["v"][g * hd:(g + 1) * hd], 1, 1, hd)
+        np.testing.assert_allclose(ao[:, h * hd:(h + 1) * hd], one, rtol=1e-12, atol=1e-12)
+
+
+def test_mirror_close_to_exact_forward():
+    """With the roundings on, every intermediate of the mirror stays within
+    four bfloat16 ulps (2^-6) of the exact forward, normwise."""
+    for seed in (7, 8):
+        cfg, w, x = _block_case(seed)
+        ref = ob.block_forward(x, w, cfg)
+        got = ob.block_forward_mirror(x, w, cfg)
+        for k in KEYS:
+            e = np.linalg.norm(got[k] - ref[k]) / np.linalg.norm(ref[k])
+            assert 0 < e <= 2.0 ** -6, (k, e)
