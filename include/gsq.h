@@ -24,7 +24,9 @@
  * Conventions for every call:
  *  - Pointers named as tensors are DEVICE pointers, allocated and owned by the
  *    caller; the library allocates and frees no memory and keeps no mutable
- *    global state. Host pointers are marked "host".
+ *    global state, except the static scratch array of
+ *    gsq_recon_loss_grad_noalloc and the per-device table of its address.
+ *    Host pointers are marked "host".
  *  - Device tensors must be 16-byte aligned (GSQ_ERR_ALIGN otherwise).
  *  - Layouts are row-major. Logits and their Lion momentum are planar
  *    [L][rows][cols] fp32 (plane k holds logit k of every coordinate), with
@@ -63,7 +65,9 @@ typedef enum {
     GSQ_ERR_ALIGN = 3,  /* a device tensor is not 16-byte aligned */
     GSQ_ERR_GRID = 4,   /* unknown grid, or a grid-specific argument missing */
     GSQ_ERR_PARAM = 5,  /* a scalar is out of range (tau, noise scale, Lion) */
-    GSQ_ERR_HIP = 6     /* the HIP runtime reported an error at launch */
+    GSQ_ERR_HIP = 6,    /* the HIP runtime reported an error at launch */
+    GSQ_ERR_SCRATCH = 7 /* gsq_recon_loss_grad_noalloc: the call needs more than
+                           the library's static scratch array holds */
 } gsq_status;
 
 /* Grids (agihunt.info summary, method paragraph). Values in scale units:
@@ -253,6 +257,30 @@ gsq_status gsq_recon_loss_grad(int32_t n_experts, const int64_t* tok_offsets,
                                const uint16_t* dW_bf16, void* workspace,
                                size_t workspace_bytes, uint16_t* RT, float* G,
                                double* loss, void* stream);
+
+/* gsq_recon_loss_grad without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Same arguments, results and
+ * kernels as gsq_recon_loss_grad (bit-identical), with the loss partials in
+ * a static device array of the library instead of a caller workspace:
+ *  - Limit: 65536 fp32 partials (256 KiB), one per workgroup of the first
+ *    product: sum over experts with tokens of ceil(rows_per_expert/256) *
+ *    ceil(n_e/256) (a single layer whose last round of tiles is split may
+ *    use up to twice that). A call that needs more returns GSQ_ERR_SCRATCH
+ *    and launches nothing; use gsq_recon_loss_grad then.
+ *  - Each device holds its own copy of the array until the process ends; the
+ *    library looks up its address on the first call on a device (the
+ *    current device, which must be the device of `stream`) and keeps it.
+ *    That first call may return GSQ_ERR_HIP if the lookup fails.
+ *  - The call allocates nothing and needs no clearing (every partial is
+ *    written before it is read within the call).
+ *  - Calls that overlap in time on one device (on different streams) share
+ *    the array and race; serialise them (one stream, or events). */
+gsq_status gsq_recon_loss_grad_noalloc(int32_t n_experts, const int64_t* tok_offsets,
+                                       int64_t rows_per_expert, int64_t cols,
+                                       const uint16_t* X, const uint16_t* XT,
+                                       const uint16_t* dW_bf16, uint16_t* RT, float* G,
+                                       double* loss, void* stream);
 
 /* Per-expert transpose of the calibration tokens: XT block e = X_e^T (see
  * gsq_recon_loss_grad for the layout). Done once per layer. */

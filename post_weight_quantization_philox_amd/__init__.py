@@ -20,7 +20,7 @@ __all__ = [
     "gsq_gptq_workspace_bytes", "gsq_init_gptq", "gsq_matmul_nt_bf16", "gsq_rmsnorm_bf16",
     "gsq_softmax_causal_bf16", "gsq_silu_mul_bf16", "gsq_add_bf16", "gsq_dequant_bf16",
     "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
-    "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes", "gsq_recon_gram",
+    "gsq_recon_loss_grad_noalloc", "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes", "gsq_recon_gram",
     "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd", "gsq_harden_pack", "gsq_noise_dump",
 ]
 
@@ -37,7 +37,7 @@ EXPORTS = ("gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn"
            "gsq_rmsnorm_bf16", "gsq_softmax_causal_bf16", "gsq_silu_mul_bf16", "gsq_add_bf16",
            "gsq_dequant_bf16",
            "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
-           "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes",
+           "gsq_recon_loss_grad_noalloc", "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes",
            "gsq_recon_gram", "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd",
            "gsq_harden_pack", "gsq_noise_dump")
 
@@ -110,6 +110,8 @@ def lib() -> ctypes.CDLL:
                                                         ctypes.c_int64]),
         "gsq_recon_loss_grad": (st, [ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                      _P, _P, ctypes.c_size_t, _P, _P, _P, _P]),
+        "gsq_recon_loss_grad_noalloc": (st, [ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64,
+                                             _P, _P, _P, _P, _P, _P, _P]),
         "gsq_transpose_tokens": (st, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
         "gsq_gram": (st, [ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
         "gsq_recon_gram_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
@@ -258,6 +260,15 @@ def gsq_recon_loss_grad(n_experts: int, tok_offsets, rows_per_expert: int, cols:
            lib().gsq_recon_loss_grad(n_experts, p, rows_per_expert, cols, _ptr(X), _ptr(XT),
                                      _ptr(dW_bf16), _ptr(workspace), workspace_bytes, _ptr(RT),
                                      _ptr(G), _ptr(loss), _stream(stream)))
+
+
+def gsq_recon_loss_grad_noalloc(n_experts: int, tok_offsets, rows_per_expert: int, cols: int, X,
+                                XT, dW_bf16, RT, G, loss, stream=None):
+    arr, p = _offsets(tok_offsets)
+    _check("gsq_recon_loss_grad_noalloc",
+           lib().gsq_recon_loss_grad_noalloc(n_experts, p, rows_per_expert, cols, _ptr(X),
+                                             _ptr(XT), _ptr(dW_bf16), _ptr(RT), _ptr(G),
+                                             _ptr(loss), _stream(stream)))
 
 
 def gsq_transpose_tokens(n_experts: int, tok_offsets, cols: int, X, XT, stream=None):

@@ -3,8 +3,16 @@
 // call has no side effect.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "gsq_internal.hpp"
+
+// Loss partials of gsq_recon_loss_grad_noalloc: a static device array
+// (each device holds its own copy until the process ends). Host code never
+// passes the array's name to a kernel: that name is a host-side stand-in, so
+// the device address is looked up once per device and kept.
+constexpr size_t kScratchFloats = size_t(1) << 16;   // 256 KiB
+static __device__ __align__(256) float scratch[kScratchFloats];
 
 namespace {
 
@@ -106,6 +114,26 @@ inline bool gemm_operand_fits(int64_t rows, int64_t ld, int64_t contraction) {
     return rows * ld * 2 <= int64_t(0x7FFFFF00) - 2 * contraction;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call there, with that device current).
+gsq_status scratch_on_current_device(float** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GSQ_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return GSQ_ERR_HIP;
+        g_scratch_dev[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return GSQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,6 +149,7 @@ const char* gsq_status_str(int status) {
         case GSQ_ERR_GRID: return "GSQ_ERR_GRID";
         case GSQ_ERR_PARAM: return "GSQ_ERR_PARAM";
         case GSQ_ERR_HIP: return "GSQ_ERR_HIP";
+        case GSQ_ERR_SCRATCH: return "GSQ_ERR_SCRATCH";
         default: return "GSQ_ERR_UNKNOWN";
     }
 }
@@ -286,6 +315,31 @@ gsq_status gsq_recon_loss_grad(int32_t n_experts, const int64_t* tok_offsets,
         return GSQ_ERR_SHAPE;
     return hip_status(gsq::launch_recon(n_experts, tok_offsets, rows_per_expert, cols, X, XT,
                                         dW_bf16, static_cast<float*>(workspace), RT, G, loss,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_recon_loss_grad_noalloc(int32_t n_experts, const int64_t* tok_offsets,
+                                       int64_t rows_per_expert, int64_t cols, const uint16_t* X,
+                                       const uint16_t* XT, const uint16_t* dW_bf16, uint16_t* RT,
+                                       float* G, double* loss, void* stream) {
+    GSQ_TRY(check_offsets(n_experts, tok_offsets, rows_per_expert, cols));
+    const bool any_tokens = tok_offsets[n_experts] > 0;
+    if (any_tokens) {
+        GSQ_TRY(need(X));
+        GSQ_TRY(need(XT));
+        GSQ_TRY(need(RT));
+    }
+    GSQ_TRY(need(dW_bf16));
+    GSQ_TRY(need(G));
+    GSQ_TRY(need(loss));
+    if (gsq::recon_partials(n_experts, tok_offsets, rows_per_expert) > kScratchFloats)
+        return GSQ_ERR_SCRATCH;
+    float* partials = nullptr;
+    GSQ_TRY(scratch_on_current_device(&partials));
+    // Every partial is written by the first product before the second reads
+    // it, so nothing in the array needs clearing.
+    return hip_status(gsq::launch_recon(n_experts, tok_offsets, rows_per_expert, cols, X, XT,
+                                        dW_bf16, partials, RT, G, loss,
                                         static_cast<hipStream_t>(stream)));
 }
 

@@ -225,3 +225,17 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), fn
                 assert "oracle/" not in text, fn
+
+
+def test_noalloc_validation(L):
+    """The allocation-free reconstruction call checks its arguments like the
+    workspace call and rejects a problem whose loss partials exceed its
+    static array before touching a device."""
+    offs = np.array([0, 2 * 65536], dtype=np.int64)
+    p = offs.ctypes.data
+    f = L.gsq_recon_loss_grad_noalloc
+    assert f(1, p, 65536, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 7
+    assert g.gsq_status_str(7) == "GSQ_ERR_SCRATCH"
+    assert f(1, p, 65536, 128, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == ERR_NULL
+    assert f(1, p, 65536, 200, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert f(1, p, 65536, 128, FAKE, FAKE, FAKE, FAKE, FAKE_MISALIGNED, FAKE, None) == ERR_ALIGN
