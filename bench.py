@@ -2,17 +2,21 @@
 
 A step is one pass of the whole hot path over the layer: relaxed forward
 (soft weights, dW), reconstruction loss and gradient (two bf16 MFMA
-products), relaxed backward with the fused Lion update. The workload is a
-Llama-3.1-8B-shaped q_proj: W 4096x4096 bf16 ~N(0, 0.02^2), 2-bit grid with
-four fp32 logits per weight, group-128 scales, 4096 calibration tokens of
-bf16 N(0,1) activations with 1 % outlier channels x20, Lion lr 1e-3.
+products), relaxed backward with the fused Lion update. The headline
+workload is the largest one that fits one GPU: a mixture-of-experts batch of
+64 experts, each W 2048x7168 bf16 ~N(0, 0.02^2) on the 2-bit grid (four fp32
+logits per weight, group-128 scales), each with its own routed calibration
+tokens (counts drawn from Zipf(1.1) on [64, 1024], bf16 N(0,1) rows of 7168),
+Lion lr 1e-3; the reconstruction products run as one grouped launch each.
 
 Prints one JSON line: weights/s over the timed steps, per-call times from HIP
 events recorded on the launch stream, the roofline of the dominant kernel,
-and the CPU oracle's rate on a bounded sample of the same workload.
-``--workload`` times one of the other synthetic layers instead (ternary
-down_proj, 3-bit local-shift gate_proj, the 64-expert batch, the 512x512
-layer); the default is the q_proj layer above.
+the CPU oracle's rate on a bounded sample of the same workload, and the same
+step measured on the other synthetic layers (``variants``: the Llama-3.1-8B
+q_proj and down_proj shapes and the 70B gate_proj shape).
+``--workload`` makes another layer the headline. ``--traffic`` turns two
+rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE) of this script into the
+per-launch HBM bytes under ``profiles/`` (no GPU needed for that step).
 """
 
 from __future__ import annotations
@@ -29,22 +33,26 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
-WORKLOAD = "qproj4096_int2"
+WORKLOAD = "moe64x2048x7168_int2"
+VARIANTS = ("qproj4096_int2", "downproj4096x14336_ternary", "gateproj28672x8192_int3local")
 N_LOGITS = {0: 4, 1: 2, 2: 5, 3: 8}    # 2-bit, ternary, 3-bit local shift, full 3-bit
 
 
 def bytes_per_coord(grid: int, w_bf16: bool) -> dict:
-    """Algorithmic bytes per weight coordinate per call. Forward: L fp32
-    logits + W read, dW (bf16) written. Backward + Lion: G, L logits and L
-    momenta read, L logits and L momenta written. The fused backward + next
-    forward adds W and dW. Local shift also reads its 1-byte warm-start code
-    (once in the fused pass). Group scale traffic (< 0.2 B) is left out.
-    2-bit bf16: 20 / 68 / 72 B."""
+    """Bytes per weight coordinate per call. Forward: L fp32 logits + W read,
+    dW (bf16) written. Backward + Lion: G, L logits and L momenta read, L
+    logits and L momenta written. The fused backward + next forward adds W
+    and dW. Local shift also reads its 1-byte warm-start code (once in the
+    fused pass). Group scale traffic (< 0.2 B) is left out. 2-bit bf16:
+    20 / 68 / 72 B. ``step`` is the relax work of one step as the method
+    defines it (forward + backward + Lion, each reading its own inputs:
+    fwd + bwd, 88 B at 2-bit bf16), which the fused pass does while moving
+    ``fused`` bytes."""
     L = N_LOGITS[grid]
     wb = 2 if w_bf16 else 4
     code = 1 if grid == 2 else 0
-    return {"fwd": 4 * L + wb + 2 + code, "bwd": 4 + 16 * L + code,
-            "fused": 4 + 16 * L + wb + 2 + code}
+    fwd, bwd = 4 * L + wb + 2 + code, 4 + 16 * L + code
+    return {"fwd": fwd, "bwd": bwd, "fused": 4 + 16 * L + wb + 2 + code, "step": fwd + bwd}
 
 
 def traffic_file(workload: str) -> str:
@@ -52,7 +60,8 @@ def traffic_file(workload: str) -> str:
 
 
 # The sources the relax kernels (the dominant kernel's family) are built from.
-RELAX_SOURCES = ("gsq_device.hpp", "gsq_internal.hpp", "relax.hip")
+RELAX_SOURCES = ("gsq_device.hpp", "gsq_internal.hpp", "relax_device.hpp", "relax.hip",
+                 "fused.hip")
 
 
 def kernel_source_hash() -> str:
@@ -62,20 +71,6 @@ def kernel_source_hash() -> str:
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()[:16]
-
-
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed counter runs, if they were
-    taken on the current kernel sources."""
-    try:
-        with open(traffic_file(workload)) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("source_hash") != kernel_source_hash():
-        return None
-    k = t.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
 
 
 def host_info() -> dict:
@@ -100,31 +95,58 @@ def host_info() -> dict:
             "thread_env": env}
 
 
-def cpu_baseline(data, rows: int):
-    """The oracle (NumPy fp64) on the first ``rows`` rows of a dense layer:
-    one full step (relaxed forward, both products against all tokens,
-    backward, Lion on logits and scales)."""
-    import numpy as np
-    import oracle
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:            # threadpoolctl missing: report one thread
-        blas_threads = 1
+        return 1
+
+
+def cpu_baseline(data, rows: int = 0, experts: int = 0):
+    """The oracle (NumPy fp64) on a bounded sample of the workload: one full
+    step (relaxed forward, both products, backward, Lion on logits and
+    scales) on the first ``rows`` rows of a dense layer against all its
+    tokens, or on the first ``experts`` whole experts of a batch, each
+    against its own routed tokens (its rows placed at their rows in the
+    batch for the noise counters)."""
+    import numpy as np
+    import oracle
+    blas_threads = _blas_threads()
     wl = data["workload"]
-    W = data["W"][:rows]
     X = data["X"]
-    scales, codes, logits = oracle.init_rtn(W, wl.grid)
-    state = {"logits": logits, "mom": np.zeros_like(logits), "scales": scales,
-             "scale_mom": np.zeros_like(scales), "codes": codes}
-    t0 = time.perf_counter()
-    oracle.step(state, W, X, wl.grid, 0, 1.0, 0, 0, 1e-3, 1e-5, bf16_dW=True)
-    dt = time.perf_counter() - t0
-    return {"value": rows * W.shape[1] / dt, "unit": "weights/s", "cores": blas_threads,
+    if wl.experts > 1:
+        rpe = wl.rows_per_expert
+        offs = data["tok_offsets"]
+        n_w, dt, toks = 0, 0.0, 0
+        for e in range(experts):
+            W = data["W"][e * rpe:(e + 1) * rpe]
+            Xe = X[offs[e]:offs[e + 1]]
+            scales, codes, logits = oracle.init_rtn(W, wl.grid)
+            state = {"logits": logits, "mom": np.zeros_like(logits), "scales": scales,
+                     "scale_mom": np.zeros_like(scales), "codes": codes}
+            t0 = time.perf_counter()
+            oracle.step(state, W, Xe, wl.grid, 0, 1.0, 0, 0, 1e-3, 1e-5, bf16_dW=True,
+                        row0=e * rpe)
+            dt += time.perf_counter() - t0
+            n_w += W.size
+            toks += Xe.shape[0]
+        sample = (f"one full step on experts 0..{experts - 1} of the {wl.experts}-expert batch "
+                  f"({n_w} weights, {toks} routed tokens in all), {dt:.1f} s")
+    else:
+        W = data["W"][:rows]
+        scales, codes, logits = oracle.init_rtn(W, wl.grid)
+        state = {"logits": logits, "mom": np.zeros_like(logits), "scales": scales,
+                 "scale_mom": np.zeros_like(scales), "codes": codes}
+        t0 = time.perf_counter()
+        oracle.step(state, W, X, wl.grid, 0, 1.0, 0, 0, 1e-3, 1e-5, bf16_dW=True)
+        dt = time.perf_counter() - t0
+        n_w = W.size
+        sample = (f"one full step on rows 0..{rows - 1} of the {wl.rows}x{wl.cols} layer "
+                  f"({n_w} weights) against all {X.shape[0]} tokens, {dt:.1f} s")
+    return {"value": n_w / dt, "unit": "weights/s", "cores": blas_threads,
             "kind": "oracle", "host": host_info(),
-            "sample": f"one full step on rows 0..{rows - 1} of the {wl.rows}x{wl.cols} layer "
-                      f"({rows * W.shape[1]} weights) against all {X.shape[0]} tokens, {dt:.1f} s; "
-                      f"NumPy elementwise work on one thread, BLAS on {blas_threads}"}
+            "sample": sample + f"; NumPy elementwise work on one thread, BLAS on {blas_threads}"}
 
 
 def describe(wl) -> str:
@@ -158,9 +180,12 @@ def spin_up(step_fn):
 
 
 def time_fused(solver, taus, warmup: int, steps: int, stream):
-    """Fused-step timing loop: returns (elapsed s, mean recon ms, mean fused
-    backward+forward ms). Step t = objective of step t (dW from the previous
-    pass) + backward and Lion of step t fused with the forward of step t + 1."""
+    """Fused-step timing loop: returns (elapsed s, mean ms of the first call,
+    mean ms of the second). Step t = objective of step t (dW from the
+    previous pass) + backward and Lion of step t fused with the forward of
+    step t + 1. With the solver's fused product (``solver.fuse``) the calls
+    are the first product (R^T) and the second product fused with the
+    backward; otherwise both products, then the fused relax pass."""
     import numpy as np
     import torch
     # The spin-up steps change the state; the timed steps start from the
@@ -180,15 +205,20 @@ def time_fused(solver, taus, warmup: int, steps: int, stream):
         t = warmup + i
         e = ev[i]
         e[0].record(stream)
-        solver.recon()
-        e[1].record(stream)
-        solver.relax_bwd_lion_fwd(t, taus[t], t + 1, taus[t + 1])
+        if solver.fuse:
+            solver.recon_residual()
+            e[1].record(stream)
+            solver.recon_bwd_lion_fwd(t, taus[t], taus[t + 1])
+        else:
+            solver.recon()
+            e[1].record(stream)
+            solver.relax_bwd_lion_fwd(t, taus[t], t + 1, taus[t + 1])
         e[2].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    rec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    fus_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    return elapsed, rec_ms, fus_ms
+    first_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    second_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    return elapsed, first_ms, second_ms
 
 
 def block_bench(args, dev):
@@ -209,11 +239,12 @@ def block_bench(args, dev):
     w["g_mlp"] = torch.ones(cfg.hidden, device=dev)
     x = torch.randn((4096, cfg.hidden), generator=gen, device=dev).to(torch.bfloat16)
     lion = g.GsqLion.make(lr_logit=1e-3, lr_scale=1e-5)
-    staged_quantize(cfg, w, x[:256], g.GRID_INT2, 2, lion, recon=args.block_recon)   # warm up
+    staged_quantize(cfg, w, x[:256], g.GRID_INT2, 2, lion, recon=args.block_recon,
+                    objective=args.block_objective)   # warm up
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     _, info = staged_quantize(cfg, w, x, g.GRID_INT2, args.block_steps, lion,
-                              recon=args.block_recon)
+                              recon=args.block_recon, objective=args.block_objective)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     n_w = sum(o * i for o, i in cfg.shapes().values())
@@ -224,98 +255,160 @@ def block_bench(args, dev):
         "dtype": "f32 relax+Lion, bf16 MFMA (fp32 accumulate), bf16 block forward",
         "config": {"workload": "Llama-3.1-8B-shaped decoder block (hidden 4096, 32 heads, 8 kv "
                                "heads, MLP 14336), random weights, 4096 tokens N(0,1), 2-bit grid",
-                   "weights": n_w, "recon": args.block_recon},
+                   "weights": n_w, "recon": args.block_recon,
+                   "objective": args.block_objective},
         "stages": {k: {"seconds": v["seconds"], "recon": v["recon"]} for k, v in info.items()},
     }), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=0,
-                    help="rows of the oracle sample (default: about 1.4e11 flops of products)")
-    ap.add_argument("--workload", default=WORKLOAD,
-                    help="synthetic layer: linear512_int2, qproj4096_int2 (default), "
-                         "downproj4096x14336_ternary, gateproj28672x8192_int3local, "
-                         "gateproj28672x8192_int3full, moe64x2048x7168_int2")
-    ap.add_argument("--block", action="store_true",
-                    help="time GSQ's staged schedule over one Llama-3.1-8B-shaped decoder block "
-                         "(random weights, 4096 tokens) instead of the per-layer step")
-    ap.add_argument("--block-steps", type=int, default=50)
-    ap.add_argument("--block-recon", default="auto", choices=("direct", "gram", "auto"),
-                    help="reconstruction form per layer in --block: the two direct products, "
-                         "the Gram form, or whichever needs fewer flops (default)")
-    ap.add_argument("--init", choices=("rtn", "gptq"), default="rtn",
-                    help="warm start; GPTQ's set-up time is reported under 'setup' (not in the step)")
-    ap.add_argument("--unfused", action="store_true",
-                    help="time separate forward and backward calls instead of the fused pass")
-    ap.add_argument("--no-variants", action="store_true",
-                    help="skip the Gram-form variant measured after the headline step")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: the step shards by output rows with no "
-              f"communication, so --gpus {args.gpus} is not run here", file=sys.stderr)
-        sys.exit(2)
+def _kernel_names():
+    """rocprofv3 kernel-name prefixes of the step's calls."""
+    return {"relax_bwd_lion_fwd": "relax_bwd_lion_kernel", "relax_fwd": "relax_fwd_kernel",
+            "relax_bwd_lion": "relax_bwd_lion_kernel"}
 
+
+def write_traffic(workload: str, fetch_dir: str, write_dir: str):
+    """HBM bytes per launch of every kernel of a workload's bench run, from
+    two rocprofv3 counter runs of ``bench.py --workload W`` (``--pmc
+    FETCH_SIZE``, then ``--pmc WRITE_SIZE``; both in KiB per dispatch).
+    Each counter is scaled by what it reads for the run's calibration copy
+    (``neg`` of a 256 MiB fp32 tensor into another: 256 MiB read, 256 MiB
+    written). Writes ``profiles/traffic_<workload>.json`` with the hash of
+    the relax kernels' sources."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        acc = {}
+        for fn in files:
+            with open(fn) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return acc
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    cal = [k for k in fetch if "neg_kernel" in k]
+    if len(cal) != 1:
+        raise SystemExit(f"calibration copy not found once among the kernels: {cal}")
+    true_kib = 256 * 1024.0
+    ff = true_kib / (sum(fetch[cal[0]]) / len(fetch[cal[0]]))
+    wf = true_kib / (sum(write[cal[0]]) / len(write[cal[0]]))
+    out = {"source_hash": kernel_source_hash(), "fetch_factor": ff, "write_factor": wf,
+           "calibration": "neg of a 256 MiB fp32 tensor (256 MiB read, 256 MiB written)",
+           "command": (f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o pmc -- python3 bench.py "
+                       f"--workload {workload} --steps 3 --warmup 1 --no-variants --no-cpu-baseline "
+                       f"--no-ab; the same with --pmc WRITE_SIZE -d {write_dir}; then python3 "
+                       f"bench.py --workload {workload} --traffic {fetch_dir} {write_dir}"),
+           "kernels": {}}
+    for k in sorted(set(fetch) & set(write)):
+        fk = sum(fetch[k]) / len(fetch[k])
+        wk = sum(write[k]) / len(write[k])
+        out["kernels"][k] = {"dispatches": len(fetch[k]), "fetch_kib_raw": fk, "write_kib_raw": wk,
+                             "bytes_per_launch": 1024.0 * (fk * ff + wk * wf)}
+    with open(traffic_file(workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(traffic_file(workload))
+
+
+def measured_kernel_traffic(workload: str, call: str):
+    """Counter bytes per launch of the kernel behind a bench call (the
+    fused pass: the relax_bwd_lion kernel instantiated with the next
+    forward), or None if no counter run matches the current sources."""
+    try:
+        with open(traffic_file(workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    if call in t.get("kernels", {}):                 # older files: keyed by call
+        return t["kernels"][call].get("bytes_per_launch")
+    # Template arguments: relax_bwd_lion_kernel<grid, debug, next forward, ...>,
+    # recon_relax_kernel<grid, next forward, ...>.
+    import re
+    want = {"relax_bwd_lion_fwd": r"relax_bwd_lion_kernel<\d+, false, true,",
+            "relax_bwd_lion": r"relax_bwd_lion_kernel<\d+, false, false,",
+            "recon_bwd_lion_fwd": r"recon_relax_kernel<\d+, true,",
+            "relax_fwd": r"relax_fwd_kernel<"}.get(call)
+    if want is None:
+        return None
+    hits = [v for k, v in t.get("kernels", {}).items() if re.search(want, k)]
+    return hits[0]["bytes_per_launch"] if len(hits) == 1 else None
+
+
+def load_workload(name: str, dev):
     import numpy as np
     import torch
     import synthetic
-    import post_weight_quantization_philox_amd as g
-    from post_weight_quantization_philox_amd.solver import LayerSolver, tau_schedule
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    g.lib()
-    dev = torch.device("cuda:0")
-    if args.block:
-        block_bench(args, dev)
-        return
-    data = synthetic.generate(args.workload, seed=0)
+    t0 = time.perf_counter()
+    data = synthetic.generate(name, seed=0)
     wl = data["workload"]
     if wl.w_bf16:
         Wd = torch.from_numpy(data["W_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
     else:
         Wd = torch.from_numpy(data["W"]).to(dev)
     Xd = torch.from_numpy(data["X_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    return data, Wd, Xd, time.perf_counter() - t0
+
+
+def run_workload(name: str, args, dev, steps: int, warmup: int, headline: bool):
+    """Set up one synthetic layer (or expert batch) and time ``steps`` fused
+    steps after ``warmup`` untimed ones. Returns the measurement as a dict
+    (the caller frees the device state)."""
+    import numpy as np
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from post_weight_quantization_philox_amd.solver import LayerSolver, tau_schedule
+
+    data, Wd, Xd, gen_s = load_workload(name, dev)
+    wl = data["workload"]
     lion = g.GsqLion.make(lr_logit=wl.lr_logit, lr_scale=1e-5)
     torch.cuda.synchronize()
     t_setup = time.perf_counter()
     solver = LayerSolver(Wd, Xd, wl.grid, tok_offsets=data["tok_offsets"],
                          rows_per_expert=wl.rows_per_expert or None, seed=0, stream_id=0, lion=lion,
-                         init=args.init)
+                         init=args.init if headline else "rtn",
+                         fuse=True if (headline and args.fuse) else "auto")
     torch.cuda.synchronize()
     setup_ms = (time.perf_counter() - t_setup) * 1e3
     M, K, N = solver.rows, solver.cols, solver.tokens
     coords = M * K
     bpc = bytes_per_coord(wl.grid, wl.w_bf16)
-    FWD_BYTES_PER_COORD, BWD_BYTES_PER_COORD, FUSED_BYTES_PER_COORD = bpc["fwd"], bpc["bwd"], bpc["fused"]
 
-    # A plain copy of known size, untimed: its counter readings calibrate
-    # FETCH_SIZE / WRITE_SIZE in the profiler runs.
-    cal_src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
-    cal_dst = torch.empty_like(cal_src)
-    cal_dst.copy_(cal_src)
+    if headline:
+        # A plain copy of known size, untimed: its counter readings calibrate
+        # FETCH_SIZE / WRITE_SIZE in the profiler runs (write_traffic).
+        cal_src = torch.zeros(64 << 20, dtype=torch.float32, device=dev)
+        cal_dst = torch.empty_like(cal_src)
+        torch.neg(cal_src, out=cal_dst)
+        del cal_src, cal_dst
 
-    taus = tau_schedule(args.warmup + args.steps + 1)
+    taus = tau_schedule(warmup + steps + 1)
     stream = torch.cuda.current_stream()
     # two products of 2*n_e*rows_e*K flops per expert (N = padded token total)
     rpe = solver.rows_per_expert
     gemm_flops = 4.0 * rpe * K * float(N)
-    offs = [int(o) for o in solver.tok_offsets]
-    n_gemm = 2 * max(1, sum(1 for e in range(len(offs) - 1) if offs[e + 1] > offs[e]))
-    if args.unfused:
+    unfused = headline and args.unfused
+    separate = None
+    if unfused:
+        solver.fuse = False
+        start = solver.state()
         spin_up(lambda: solver.step(0, taus[0]))
-        for t in range(args.warmup):
+        solver.load_state(start)
+        del start
+        for t in range(warmup):
             solver.step(t, taus[t])
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            t = args.warmup + i
+        for i in range(steps):
+            t = warmup + i
             e = ev[i]
             e[0].record(stream)
             solver.relax_fwd(t, taus[t])
@@ -330,108 +423,231 @@ def main():
         rec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
         bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
         kernels = {
-            "relax_fwd": {"ms": fwd_ms, "GB/s": FWD_BYTES_PER_COORD * coords / fwd_ms / 1e6},
-            "recon_loss_grad": {"ms": rec_ms, "TFLOP/s": gemm_flops / rec_ms / 1e9,
-                                "note": "two bf16 GEMMs (2NMK flops each); GEMM2's first workgroup sums the loss"},
-            "relax_bwd_lion": {"ms": bwd_ms, "GB/s": BWD_BYTES_PER_COORD * coords / bwd_ms / 1e6},
+            "relax_fwd": {"ms": fwd_ms, "GB/s": bpc["fwd"] * coords / fwd_ms / 1e6},
+            "recon_loss_grad": {"ms": rec_ms, "TFLOP/s": gemm_flops / rec_ms / 1e9},
+            "relax_bwd_lion": {"ms": bwd_ms, "GB/s": bpc["bwd"] * coords / bwd_ms / 1e6},
         }
-        per_launch = {"relax_fwd": fwd_ms, "recon_loss_grad": rec_ms / n_gemm,
-                      "relax_bwd_lion": bwd_ms}
-        bytes_per = {"relax_fwd": FWD_BYTES_PER_COORD, "relax_bwd_lion": BWD_BYTES_PER_COORD}
+        relax_call, relax_ms = "relax_bwd_lion", fwd_ms + bwd_ms
+        moved = bpc["fwd"] + bpc["bwd"]
+    elif solver.fuse:
+        elapsed, rec1_ms, fus_ms = time_fused(solver, taus, warmup, steps, stream)
+        moved = bpc["fused"] - 4                     # no G read
+        kernels = {
+            "recon_residual": {"ms": rec1_ms, "TFLOP/s": gemm_flops / 2 / rec1_ms / 1e9,
+                               "note": "first product R^T = dW X^T (2NMK flops; one grouped "
+                                       "launch for an expert batch) and the loss partials"},
+            "recon_bwd_lion_fwd": {"ms": fus_ms, "GB/s": moved * coords / fus_ms / 1e6,
+                                   "TFLOP/s": gemm_flops / 2 / fus_ms / 1e9,
+                                   "note": "second product G = 2 R^T X formed tile by tile and "
+                                           "consumed by backward + Lion of step t and forward of "
+                                           "step t+1 (G never stored; bytes moved)"},
+        }
+        relax_call, relax_ms = "recon_bwd_lion_fwd", fus_ms
+        rec_ms = rec1_ms
     else:
-        elapsed, rec_ms, fus_ms = time_fused(solver, taus, args.warmup, args.steps, stream)
+        elapsed, rec_ms, fus_ms = time_fused(solver, taus, warmup, steps, stream)
         kernels = {
             "recon_loss_grad": {"ms": rec_ms, "TFLOP/s": gemm_flops / rec_ms / 1e9,
-                                "note": "two bf16 GEMMs (2NMK flops each); GEMM2's first workgroup sums the loss"},
-            "relax_bwd_lion_fwd": {"ms": fus_ms,
-                                   "GB/s": FUSED_BYTES_PER_COORD * coords / fus_ms / 1e6,
-                                   "note": "backward + Lion of step t and forward of step t+1"},
+                                "note": "two bf16 GEMMs (2NMK flops each; one grouped launch "
+                                        "each for an expert batch); the second sums the loss"},
+            "relax_bwd_lion_fwd": {"ms": fus_ms, "GB/s": bpc["fused"] * coords / fus_ms / 1e6,
+                                   "note": "backward + Lion of step t and forward of step t+1 "
+                                           "(bytes moved)"},
         }
-        per_launch = {"recon_loss_grad": rec_ms / n_gemm, "relax_bwd_lion_fwd": fus_ms}
-        bytes_per = {"relax_bwd_lion_fwd": FUSED_BYTES_PER_COORD}
-    loss = float(solver.loss.item())
-    ms_per_step = elapsed * 1e3 / args.steps
-
-    # Dominant single kernel: the recon call is two products of equal flops
-    # (each one launch, or two when its last round is split into 256x128
-    # tiles), so each product is weighed at its share of the call.
-    dominant = max(per_launch, key=per_launch.get)
-    if dominant == "recon_loss_grad":
-        ach = kernels[dominant]["TFLOP/s"]
-        roof = {"bound": "mfma", "kernel": "gemm_nt_kernel (both products of the call)",
-                "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
-    else:
-        per = bytes_per[dominant]
-        ach = kernels[dominant]["GB/s"]
-        roof = {"bound": "hbm", "kernel": dominant + "_kernel", "achieved": ach,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                "traffic": measured_traffic(args.workload, dominant),
-                "algorithmic_bytes_per_launch": per * coords}
-
-    out = {
-        "metric": "GSQ relax step weights/sec (fwd+recon+bwd+Lion)",
-        "value": coords * args.steps / elapsed,
-        "unit": "weights/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32 relax+Lion, bf16 MFMA (fp32 accumulate)",
-        "data": "synthetic",
-        "config": {"workload": describe(wl), "name": wl.name,
-                   "rows": M, "cols": K, "tokens": int(data["tok_offsets"][-1]),
-                   "experts": wl.experts, "grid": ["int2", "ternary", "int3_local", "int3"][wl.grid],
-                   "lion_lr": wl.lr_logit},
-        "roofline": roof,
-        "kernels": kernels,
-        "last_loss": loss,
-        "setup": {"init": args.init, "ms": setup_ms,
-                  "note": "warm start, X^T and state allocation, once per layer, not in the step"},
-    }
-    if not args.no_variants and not args.unfused and wl.experts == 1:
-        # Same step with the objective in Gram form (H = X^T X formed once,
-        # untimed; one product of 2*M*K*K flops per step instead of two of
-        # 2*N*M*K), on a fresh solver. Reported beside the headline, which
-        # keeps the two-product form.
+        relax_call, relax_ms = "relax_bwd_lion_fwd", fus_ms
+        moved = bpc["fused"]
+    if headline and not unfused and not args.no_ab:
+        # The other form of the same step, for the A/B: with the second
+        # product fused into the backward (G never stored), or with the
+        # separate calls.
+        fused = solver.fuse
+        solver.fuse = not fused
+        a_el, a_first, a_second = time_fused(solver, taus, min(warmup, 3), min(steps, 10), stream)
+        solver.fuse = fused
+        n_ab = min(steps, 10)
+        separate = ({"ms_per_step": a_el * 1e3 / n_ab, "recon_loss_grad_ms": a_first,
+                     "relax_bwd_lion_fwd_ms": a_second,
+                     "note": "the same step with G stored by the second product and read back "
+                             "by the relax pass"} if fused else
+                    {"ms_per_step": a_el * 1e3 / n_ab, "recon_residual_ms": a_first,
+                     "recon_bwd_lion_fwd_ms": a_second,
+                     "note": "the same step with the second product fused into backward + Lion "
+                             "+ next forward (gsq_recon_bwd_lion_fwd: G never stored)"})
+    ms_per_step = elapsed * 1e3 / steps
+    # Roofline of the relax work: the algorithmic bytes of one step's
+    # forward + backward + Lion (the method's per-coordinate figure) over the
+    # time of the kernel(s) that do it; beside it, the bytes the kernel moves.
+    ach = bpc["step"] * coords / relax_ms / 1e6
+    ach_moved = moved * coords / relax_ms / 1e6
+    kname = {"recon_bwd_lion_fwd": "recon_relax_kernel (second product + backward + Lion + "
+                                   "next forward)",
+             "relax_bwd_lion_fwd": "relax_bwd_lion_kernel (fused backward + Lion + next forward)",
+             "relax_bwd_lion": "relax_fwd_kernel + relax_bwd_lion_kernel"}[relax_call]
+    roof = {"bound": "hbm", "kernel": kname,
+            "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+            "traffic": measured_kernel_traffic(name, relax_call) if not unfused else None,
+            "algorithmic_bytes_per_coord": bpc["step"],
+            "algorithmic_bytes_per_launch": bpc["step"] * coords,
+            "moved_bytes_per_coord": moved, "achieved_moved": ach_moved,
+            "frac_moved": ach_moved / HBM_PEAK_GBS, "launch_ms": relax_ms}
+    gflops = gemm_flops / 2 if solver.fuse else gemm_flops     # the separate products' flops
+    gemm = {"achieved": gflops / rec_ms / 1e9, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": gflops / rec_ms / 1e9 / BF16_PEAK_TFLOPS,
+            "products": "first only (the second runs inside the fused kernel)" if solver.fuse
+            else "both"}
+    res = {"name": wl.name, "workload": describe(wl), "value": coords * steps / elapsed,
+           "ms_per_step": ms_per_step, "steps": steps, "warmup": warmup, "coords": coords,
+           "rows": M, "cols": K, "tokens": int(data["tok_offsets"][-1]), "experts": wl.experts,
+           "grid": ["int2", "ternary", "int3_local", "int3"][wl.grid], "lion_lr": wl.lr_logit,
+           "roofline": roof, "recon_mfma": gemm, "kernels": kernels, "fused_product": solver.fuse,
+           "last_loss": float(solver.loss.item()),
+           "setup": {"init": args.init if headline else "rtn", "ms": setup_ms,
+                     "inputs_drawn_s": gen_s,
+                     "note": "warm start, X^T and state allocation, once per layer, not in the step"}}
+    if separate is not None:
+        res["ab_other_path"] = separate
+    if name == "qproj4096_int2" and not unfused:
+        # The same step with the objective in Gram form (H = X^T X formed
+        # once, untimed; one product of 2*M*K*K flops per step instead of two
+        # of 2*N*M*K), on a fresh solver; then the two-product solve captured
+        # as one HIP graph.
         del solver
         torch.cuda.empty_cache()
         gsol = LayerSolver(Wd, Xd, wl.grid, seed=0, stream_id=0, recon="gram", lion=lion)
-        g_el, g_rec, g_fus = time_fused(gsol, taus, args.warmup, args.steps, stream)
+        g_el, g_rec, g_fus = time_fused(gsol, taus, warmup, steps, stream)
         gram_flops = 2.0 * M * K * K
-        out["variants"] = {"gram": {
-            "value": coords * args.steps / g_el, "unit": "weights/s",
-            "ms_per_step": g_el * 1e3 / args.steps,
+        res["gram"] = {
+            "value": coords * steps / g_el, "unit": "weights/s", "ms_per_step": g_el * 1e3 / steps,
             "recon_gram": {"ms": g_rec, "TFLOP/s": gram_flops / g_rec / 1e9,
                            "note": "one bf16 GEMM dW H (2MK^2 flops) + loss finalize"},
-            "relax_bwd_lion_fwd": {"ms": g_fus,
-                                   "GB/s": FUSED_BYTES_PER_COORD * coords / g_fus / 1e6},
-            "last_loss": float(gsol.loss.item()),
-        }}
+            "relax_bwd_lion_fwd": {"ms": g_fus, "GB/s": bpc["fused"] * coords / g_fus / 1e6},
+            "last_loss": float(gsol.loss.item())}
         del gsol
-        # The same annealed steps captured as one HIP graph (launch overhead
-        # removed; it matters for small layers), timed over one replay.
         torch.cuda.empty_cache()
         csol = LayerSolver(Wd, Xd, wl.grid, seed=0, stream_id=0, lion=lion)
-        graph = csol.capture_solve(args.steps)
+        graph = csol.capture_solve(steps)
         graph.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(3):
             graph.replay()
         torch.cuda.synchronize()
-        g_el = (time.perf_counter() - t0) / 3
-        out["variants"]["graph"] = {
-            "value": coords * args.steps / g_el, "unit": "weights/s",
-            "ms_per_step": g_el * 1e3 / args.steps,
-            "note": "the two-product step, whole K-step solve replayed as one HIP graph"}
+        c_el = (time.perf_counter() - t0) / 3
+        res["graph"] = {"value": coords * steps / c_el, "unit": "weights/s",
+                        "ms_per_step": c_el * 1e3 / steps,
+                        "note": "the two-product step, whole solve replayed as one HIP graph"}
         del csol, graph
-    if not args.no_cpu_baseline and wl.experts == 1:
-        rows = args.cpu_rows or max(64, min(M, int(4096 * 4096 * 4096 // (K * N)) // 64 * 64))
-        out["cpu_baseline"] = cpu_baseline(data, rows)
+    else:
+        del solver
+    del Wd, Xd
+    torch.cuda.empty_cache()
+    return res, data
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="dense headline: rows of the oracle sample (default: about 1.4e11 flops "
+                         "of products)")
+    ap.add_argument("--cpu-experts", type=int, default=2,
+                    help="expert-batch headline: whole experts in the oracle sample (default 2)")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="headline layer: moe64x2048x7168_int2 (default), qproj4096_int2, "
+                         "downproj4096x14336_ternary, gateproj28672x8192_int3local, "
+                         "gateproj28672x8192_int3full, linear512_int2")
+    ap.add_argument("--block", action="store_true",
+                    help="time GSQ's staged schedule over one Llama-3.1-8B-shaped decoder block "
+                         "(random weights, 4096 tokens) instead of the per-layer step")
+    ap.add_argument("--block-steps", type=int, default=50)
+    ap.add_argument("--block-recon", default="auto", choices=("direct", "gram", "auto"),
+                    help="reconstruction form per layer in --block: the two direct products, "
+                         "the Gram form, or whichever needs fewer flops (default)")
+    ap.add_argument("--block-objective", default="block", choices=("block", "layer"),
+                    help="in --block: fit the output and down projections to the full-precision "
+                         "block (default) or every layer to its own output")
+    ap.add_argument("--init", choices=("rtn", "gptq"), default="rtn",
+                    help="warm start of the headline layer; GPTQ's set-up time is reported "
+                         "under 'setup' (not in the step)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time separate forward and backward calls instead of the fused pass")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="measure the headline workload only")
+    ap.add_argument("--fuse", action="store_true",
+                    help="headline step with the second product fused into backward + Lion "
+                         "(gsq_recon_bwd_lion_fwd) instead of the separate calls")
+    ap.add_argument("--no-ab", action="store_true",
+                    help="skip timing the other form of the headline step (fused / separate)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 counter runs of this script into "
+                         "profiles/traffic_<workload>.json and exit")
+    args = ap.parse_args()
+    if args.traffic:
+        write_traffic(args.workload, *args.traffic)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the step shards by output rows with no "
+              f"communication, so --gpus {args.gpus} is not run here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import post_weight_quantization_philox_amd as g
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    g.lib()
+    dev = torch.device("cuda:0")
+    if args.block:
+        block_bench(args, dev)
+        return
+    head, data = run_workload(args.workload, args, dev, args.steps, args.warmup, headline=True)
+    wl = data["workload"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        if wl.experts > 1:
+            cpu = cpu_baseline(data, experts=max(1, min(args.cpu_experts, wl.experts)))
+        else:
+            M, K, N = wl.rows, wl.cols, int(data["tok_offsets"][-1])
+            rows = args.cpu_rows or max(64, min(M, int(4096 * 4096 * 4096 // (K * N)) // 64 * 64))
+            cpu = cpu_baseline(data, rows=rows)
+    del data
+    out = {
+        "metric": "GSQ relax step weights/sec (fwd+recon+bwd+Lion)",
+        "value": head["value"],
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "vs_baseline": None,
+        "dtype": "f32 relax+Lion, bf16 MFMA (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {k: head[k] for k in ("workload", "name", "rows", "cols", "tokens", "experts",
+                                        "grid", "lion_lr")},
+        "roofline": head["roofline"],
+        "recon_mfma": head["recon_mfma"],
+        "kernels": head["kernels"],
+        "fused_product": head["fused_product"],
+        "last_loss": head["last_loss"],
+        "setup": head["setup"],
+    }
+    if "ab_other_path" in head:
+        out["ab_other_path"] = head["ab_other_path"]
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    if not args.no_variants:
+        out["variants"] = {}
+        for name in VARIANTS:
+            if name == args.workload:
+                continue
+            res, _ = run_workload(name, args, dev, min(args.steps, 20), min(args.warmup, 5),
+                                  headline=False)
+            out["variants"][name] = res
     print(json.dumps(out), flush=True)
 
 

@@ -198,6 +198,10 @@ gsq_status gsq_silu_mul_bf16(int64_t n, const uint16_t* gate, const uint16_t* up
 gsq_status gsq_add_bf16(int64_t n, const uint16_t* a, const uint16_t* b,
                         uint16_t* out, void* stream);
 
+/* out = a - b elementwise, n elements (the offsets of the staged schedule). */
+gsq_status gsq_sub_bf16(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
+                        void* stream);
+
 /* Hard weights W = s * v(code) in bf16 from gsq_harden_pack's codes (uint8
  * [rows][cols]) and fp16 scales ([rows][cols/128]); v as in gsq_harden_pack
  * (ternary codes are t + 1; local-shift codes are final 3-bit codes). */
@@ -281,6 +285,69 @@ gsq_status gsq_recon_loss_grad_noalloc(int32_t n_experts, const int64_t* tok_off
                                        const uint16_t* X, const uint16_t* XT,
                                        const uint16_t* dW_bf16, uint16_t* RT, float* G,
                                        double* loss, void* stream);
+
+/* The objective and its gradient split differently, so that the second
+ * product can be fused with the backward (agihunt.info summary, method
+ * paragraph: the gradient of the output reconstruction error drives the
+ * logits and scales). gsq_recon_residual followed by gsq_recon_bwd_lion_fwd
+ * reproduces gsq_recon_loss_grad followed by gsq_relax_bwd_lion_fwd (or, with
+ * with_next = 0, gsq_relax_bwd_lion) bit for bit (R^T, loss, logits, momenta,
+ * scales, scale momenta, next dW), but G = 2 R^T X is formed tile by tile on
+ * the matrix cores and consumed where it is formed, never stored: 8 bytes
+ * per weight per step less HBM traffic. It pays where the second product is
+ * bound by storing G, i.e. few tokens per expert; for a dense layer with
+ * thousands of tokens the separate, MFMA-tuned product is faster.
+ *
+ * gsq_recon_residual: the first product alone, R_e^T = dW_e X_e^T (bf16) for
+ * every expert, and the loss partials (sums of R^2, one per workgroup) in
+ * `workspace`. Arguments as gsq_recon_loss_grad. */
+gsq_status gsq_recon_residual(int32_t n_experts, const int64_t* tok_offsets,
+                              int64_t rows_per_expert, int64_t cols, const uint16_t* X,
+                              const uint16_t* dW_bf16, void* workspace, size_t workspace_bytes,
+                              uint16_t* RT, void* stream);
+
+/* The second product fused with backward + Lion and, with with_next = 1, the
+ * next step's forward; the loss is summed from the partials the preceding
+ * gsq_recon_residual left in `workspace` (same experts and token offsets,
+ * same stream).
+ *   layer         the whole layer (rows = n_experts * rows per expert)
+ *   n_experts, tok_offsets, XT, RT, loss
+ *                 as gsq_recon_loss_grad (the total token count must be below
+ *                 2^31)
+ *   workspace     the workspace gsq_recon_residual filled (read only)
+ *   logits, mom, scales, scale_mom, init_codes, step, tau, noise_scale, lion
+ *                 as gsq_relax_bwd_lion (no debug outputs)
+ *   with_next     1: then the forward of next_step at next_tau on the updated
+ *                 state into dW_bf16 (W and dW_bf16 needed), as
+ *                 gsq_relax_bwd_lion_fwd; 0: backward + Lion only (the last
+ *                 step); W, next_tau and dW_bf16 are then ignored */
+gsq_status gsq_recon_bwd_lion_fwd(const gsq_layer* layer, int32_t n_experts,
+                                  const int64_t* tok_offsets, const uint16_t* XT,
+                                  const uint16_t* RT, const void* workspace,
+                                  size_t workspace_bytes, double* loss, float* logits, float* mom,
+                                  float* scales, float* scale_mom, const uint8_t* init_codes,
+                                  const void* W, uint32_t step, float tau, float noise_scale,
+                                  const gsq_lion* lion, int32_t with_next, uint32_t next_step,
+                                  float next_tau, uint16_t* dW_bf16, void* stream);
+
+/* The objective of one dense layer fitted to a target downstream of itself:
+ * R = X dW^T + E0 with E0 fixed, loss = sum R^2, G = 2 R^T X. With
+ * E0 = X W^T - Y the loss is ||X W_soft^T - Y||^2: the staged schedule
+ * (agihunt.info summary, optimizer paragraph) fits the output projection to
+ * the full-precision attention output and the MLP's last projection to the
+ * full-precision block output this way. E0 enters the first product's
+ * epilogue (one fp32 add before the square and the bf16 rounding of R^T).
+ *   rows, cols, tokens  the layer and its calibration tokens (tokens > 0, a
+ *                 multiple of 64; cols a multiple of 128)
+ *   X, XT, dW_bf16, workspace, RT, G, loss
+ *                 as gsq_recon_loss_grad with one expert
+ *                 (workspace of gsq_recon_workspace_bytes(1, {0, tokens}, ...))
+ *   E0T           [rows][tokens] bf16, E0 transposed (the layout of R^T) */
+gsq_status gsq_recon_loss_grad_offset(int64_t rows, int64_t cols, int64_t tokens,
+                                      const uint16_t* X, const uint16_t* XT,
+                                      const uint16_t* dW_bf16, const uint16_t* E0T,
+                                      void* workspace, size_t workspace_bytes, uint16_t* RT,
+                                      float* G, double* loss, void* stream);
 
 /* Per-expert transpose of the calibration tokens: XT block e = X_e^T (see
  * gsq_recon_loss_grad for the layout). Done once per layer. */

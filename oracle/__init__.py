@@ -18,6 +18,7 @@ from .gsq import (GRID_INT2, GRID_TERNARY, GRID_INT3_LOCAL, GRID_INT3, N_LOGITS,
                   CODE_BITS, LOCAL_OFFSETS, level_value, grid_levels,
                   candidate_codes, init_rtn, gptq_hessian, gptq, noise, relax_probs, ternary_terms,
                   relax_fwd, relax_bwd, recon_loss_grad,
-                  recon_loss_grad_grouped, gram, recon_loss_grad_gram, hard_loss, lion, harden, pack_codes,
+                  recon_loss_grad_grouped, recon_loss_grad_offset, gram, recon_loss_grad_gram,
+                  hard_loss, lion, harden, pack_codes,
                   unpack_codes, scales_to_f16_bits, harden_pack, tau_schedule,
                   round_bf16, step, quantize_layer)

@@ -116,3 +116,22 @@ def block_forward_mirror(x, w: dict, cfg: dict):
     act = _rb(silu_mul(f(xm, w["gate"]), f(xm, w["up"])))
     out = _rb(h_ + f(act, w["down"]))
     return {"out": out, "x_attn": xa, "x_o": ao, "h": h_, "x_mlp": xm, "x_down": act}
+
+
+def stage_offset_T(W, x_q, x_fp, resid_q=None, resid_fp=None, mirror: bool = False):
+    """Offset of a layer fitted to a full-precision target (the staged
+    schedule's value/output and MLP stages, agihunt.info optimizer
+    paragraph): E0^T = W (x_q - x_fp)^T + (resid_q - resid_fp)^T, so that
+    with R = x_q dW^T + E0 the residual of the layer with weights W + dW is
+    x_q (W + dW)^T + resid_q - (x_fp W^T + resid_fp). With ``mirror`` each
+    difference, the product and the sum are rounded to bfloat16 where the GPU
+    stores them."""
+    r = _rb if mirror else (lambda a: np.asarray(a, dtype=np.float64))
+    W = np.asarray(W, dtype=np.float64)
+    d = r(np.asarray(x_q, dtype=np.float64) - np.asarray(x_fp, dtype=np.float64))
+    E = r(W @ d.T)
+    if resid_q is not None:
+        dr = r(np.asarray(resid_q, dtype=np.float64) - np.asarray(resid_fp, dtype=np.float64))
+        E = r(E + dr.T)
+    return E
+

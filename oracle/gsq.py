@@ -363,6 +363,22 @@ def recon_loss_grad(X, dW):
     return RT, float(np.sum(RT * RT)), 2.0 * (RT @ Xd)
 
 
+def recon_loss_grad_offset(X, dW, E0T):
+    """The reconstruction objective with a fixed offset on the residual.
+
+    R = X dW^T + E0 (E0 fixed, given transposed as ``E0T`` [out, tokens]),
+    loss = sum R^2, G = dLoss/d(dW) = 2 R^T X. With E0 = X_q W^T - Y_target
+    (the layer's full-precision output on quantized inputs minus the output
+    the stage should reproduce) this is ||X_q W_soft^T - Y_target||^2: a
+    layer fitted to a target downstream of itself, the block output for the
+    MLP and the attention output for the value/output stage (agihunt.info,
+    optimizer paragraph on the staged schedule). Returns ``(RT, loss, G)``.
+    """
+    Xd = np.asarray(X, dtype=np.float64)
+    RT = np.asarray(dW, dtype=np.float64) @ Xd.T + np.asarray(E0T, dtype=np.float64)
+    return RT, float(np.sum(RT * RT)), 2.0 * (RT @ Xd)
+
+
 def recon_loss_grad_grouped(X_cat, tok_offsets, dW_cat, rows_per_expert: int):
     """Sum over experts of the per-expert reconstruction objective.
 
@@ -550,7 +566,7 @@ def step(state: dict, W, X, grid: int, t: int, tau: float, seed: int,
          stream: int, lr_logit: float, lr_scale: float, beta1: float = 0.9,
          beta2: float = 0.99, weight_decay: float = 0.0,
          noise_scale: float = 1.0, bf16_dW: bool = False, group: int = 128,
-         bf16_RT: bool = False, H=None, row0: int = 0):
+         bf16_RT: bool = False, H=None, row0: int = 0, E0T=None):
     """One full relaxed-quantization step on a whole layer, in place on
     ``state`` (``logits``, ``mom``, ``scales``, ``scale_mom``, ``codes``).
     ``row0`` places the rows given at that row of a larger layer (it only
@@ -561,7 +577,8 @@ def step(state: dict, W, X, grid: int, t: int, tau: float, seed: int,
     the products and ``bf16_RT`` rounds R^T to bfloat16 before forming G, as
     a bf16 matrix engine consumes them (the loss stays the exact sum of R^2).
     With a Gram matrix ``H`` (see :func:`gram`) the objective is taken in Gram
-    form instead and X is not used. Returns the loss.
+    form instead and X is not used; with ``E0T`` the residual carries that
+    fixed offset (:func:`recon_loss_grad_offset`). Returns the loss.
     """
     codes = state["codes"] if grid == GRID_INT3_LOCAL else None
     f = relax_fwd(state["logits"], state["scales"], W, grid, seed, stream, t,
@@ -570,7 +587,8 @@ def step(state: dict, W, X, grid: int, t: int, tau: float, seed: int,
     if H is not None:
         loss, G = recon_loss_grad_gram(dW, H)
     else:
-        RT, loss, G = recon_loss_grad(X, dW)
+        RT, loss, G = (recon_loss_grad(X, dW) if E0T is None
+                       else recon_loss_grad_offset(X, dW, E0T))
         if bf16_RT:
             G = 2.0 * (round_bf16(RT).astype(np.float64) @ np.asarray(X, dtype=np.float64))
     gl, gs = relax_bwd(G, state["logits"], state["scales"], grid, seed, stream,

@@ -18,9 +18,12 @@ __all__ = [
     "GsqError", "GsqLayer", "GsqLion", "lib", "exported_symbols",
     "gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
     "gsq_gptq_workspace_bytes", "gsq_init_gptq", "gsq_matmul_nt_bf16", "gsq_rmsnorm_bf16",
-    "gsq_softmax_causal_bf16", "gsq_silu_mul_bf16", "gsq_add_bf16", "gsq_dequant_bf16",
+    "gsq_softmax_causal_bf16", "gsq_silu_mul_bf16", "gsq_add_bf16", "gsq_sub_bf16",
+    "gsq_dequant_bf16", "gsq_recon_loss_grad_offset",
     "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
-    "gsq_recon_loss_grad_noalloc", "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes", "gsq_recon_gram",
+    "gsq_recon_loss_grad_noalloc", "gsq_recon_residual", "gsq_recon_bwd_lion_fwd",
+    "gsq_transpose_tokens", "gsq_gram",
+    "gsq_recon_gram_workspace_bytes", "gsq_recon_gram",
     "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd", "gsq_harden_pack", "gsq_noise_dump",
 ]
 
@@ -35,10 +38,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsq.so")
 EXPORTS = ("gsq_abi_version", "gsq_status_str", "gsq_num_logits", "gsq_init_rtn",
            "gsq_gptq_workspace_bytes", "gsq_init_gptq", "gsq_matmul_nt_bf16",
            "gsq_rmsnorm_bf16", "gsq_softmax_causal_bf16", "gsq_silu_mul_bf16", "gsq_add_bf16",
-           "gsq_dequant_bf16",
+           "gsq_sub_bf16", "gsq_dequant_bf16", "gsq_recon_loss_grad_offset",
            "gsq_relax_fwd", "gsq_recon_workspace_bytes", "gsq_recon_loss_grad",
-           "gsq_recon_loss_grad_noalloc", "gsq_transpose_tokens", "gsq_gram", "gsq_recon_gram_workspace_bytes",
-           "gsq_recon_gram", "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd",
+           "gsq_recon_loss_grad_noalloc", "gsq_recon_residual", "gsq_recon_bwd_lion_fwd",
+           "gsq_transpose_tokens",
+           "gsq_gram", "gsq_recon_gram_workspace_bytes", "gsq_recon_gram", "gsq_relax_bwd_lion", "gsq_relax_bwd_lion_fwd",
            "gsq_harden_pack", "gsq_noise_dump")
 
 
@@ -101,6 +105,9 @@ def lib() -> ctypes.CDLL:
         "gsq_softmax_causal_bf16": (st, [ctypes.c_int64, _P, ctypes.c_float, _P, _P]),
         "gsq_silu_mul_bf16": (st, [ctypes.c_int64, _P, _P, _P, _P]),
         "gsq_add_bf16": (st, [ctypes.c_int64, _P, _P, _P, _P]),
+        "gsq_sub_bf16": (st, [ctypes.c_int64, _P, _P, _P, _P]),
+        "gsq_recon_loss_grad_offset": (st, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                            _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _P]),
         "gsq_dequant_bf16": (st, [_L, _P, _P, _P, _P]),
         "gsq_init_gptq": (st, [_L, _P, ctypes.c_int64, _P, ctypes.c_float, ctypes.c_float, _P,
                                ctypes.c_size_t, _P, _P, _P, _P, _P]),
@@ -112,6 +119,12 @@ def lib() -> ctypes.CDLL:
                                      _P, _P, ctypes.c_size_t, _P, _P, _P, _P]),
         "gsq_recon_loss_grad_noalloc": (st, [ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64,
                                              _P, _P, _P, _P, _P, _P, _P]),
+        "gsq_recon_residual": (st, [ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                    _P, ctypes.c_size_t, _P, _P]),
+        "gsq_recon_bwd_lion_fwd": (st, [_L, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P,
+                                        _P, _P, _P, _P, _P, _P, ctypes.c_uint32, ctypes.c_float,
+                                        ctypes.c_float, ctypes.POINTER(GsqLion), ctypes.c_int32,
+                                        ctypes.c_uint32, ctypes.c_float, _P, _P]),
         "gsq_transpose_tokens": (st, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
         "gsq_gram": (st, [ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
         "gsq_recon_gram_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
@@ -234,6 +247,20 @@ def gsq_add_bf16(n: int, a, b, out, stream=None):
     _check("gsq_add_bf16", lib().gsq_add_bf16(n, _ptr(a), _ptr(b), _ptr(out), _stream(stream)))
 
 
+def gsq_sub_bf16(n: int, a, b, out, stream=None):
+    _check("gsq_sub_bf16", lib().gsq_sub_bf16(n, _ptr(a), _ptr(b), _ptr(out), _stream(stream)))
+
+
+def gsq_recon_loss_grad_offset(rows: int, cols: int, tokens: int, X, XT, dW_bf16, E0T, workspace,
+                               RT, G, loss, stream=None, workspace_bytes=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("gsq_recon_loss_grad_offset",
+           lib().gsq_recon_loss_grad_offset(rows, cols, tokens, _ptr(X), _ptr(XT), _ptr(dW_bf16),
+                                            _ptr(E0T), _ptr(workspace), workspace_bytes, _ptr(RT),
+                                            _ptr(G), _ptr(loss), _stream(stream)))
+
+
 def gsq_dequant_bf16(layer: GsqLayer, codes, scales_f16, W, stream=None):
     _check("gsq_dequant_bf16", lib().gsq_dequant_bf16(ctypes.byref(layer), _ptr(codes),
                                                       _ptr(scales_f16), _ptr(W), _stream(stream)))
@@ -269,6 +296,32 @@ def gsq_recon_loss_grad_noalloc(n_experts: int, tok_offsets, rows_per_expert: in
            lib().gsq_recon_loss_grad_noalloc(n_experts, p, rows_per_expert, cols, _ptr(X),
                                              _ptr(XT), _ptr(dW_bf16), _ptr(RT), _ptr(G),
                                              _ptr(loss), _stream(stream)))
+
+
+def gsq_recon_residual(n_experts: int, tok_offsets, rows_per_expert: int, cols: int, X, dW_bf16,
+                       workspace, RT, stream=None, workspace_bytes=None):
+    arr, p = _offsets(tok_offsets)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("gsq_recon_residual",
+           lib().gsq_recon_residual(n_experts, p, rows_per_expert, cols, _ptr(X), _ptr(dW_bf16),
+                                    _ptr(workspace), workspace_bytes, _ptr(RT), _stream(stream)))
+
+
+def gsq_recon_bwd_lion_fwd(layer: GsqLayer, n_experts: int, tok_offsets, XT, RT, workspace, loss,
+                           logits, mom, scales, scale_mom, init_codes, W, step: int, tau: float,
+                           noise_scale: float, lion: GsqLion, with_next: bool, next_step: int,
+                           next_tau: float, dW_bf16, stream=None, workspace_bytes=None):
+    arr, p = _offsets(tok_offsets)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("gsq_recon_bwd_lion_fwd",
+           lib().gsq_recon_bwd_lion_fwd(ctypes.byref(layer), n_experts, p, _ptr(XT), _ptr(RT),
+                                        _ptr(workspace), workspace_bytes, _ptr(loss), _ptr(logits),
+                                        _ptr(mom), _ptr(scales), _ptr(scale_mom), _ptr(init_codes),
+                                        _ptr(W), step, tau, noise_scale, ctypes.byref(lion),
+                                        1 if with_next else 0, next_step, next_tau, _ptr(dW_bf16),
+                                        _stream(stream)))
 
 
 def gsq_transpose_tokens(n_experts: int, tok_offsets, cols: int, X, XT, stream=None):

@@ -16,7 +16,17 @@ Readings: query and key are quantized together as one row-stacked layer (they
 see the same input); the value/output stage quantizes V, then O on the
 attention output recomputed with the quantized Q, K and V; gate and up are
 quantized together, then down on the SwiGLU activations recomputed with the
-quantized gate and up.
+quantized gate and up. With ``objective="block"`` (the default) the two
+stage-closing projections are fitted to full-precision targets rather than to
+their own outputs: O to the full-precision block's attention output, so it
+absorbs the error the quantized Q, K and V leave (value/output jointly), and
+down to the full-precision block output (the MLP on the block output). Each
+is the layer objective with a fixed offset on the residual,
+R = X dW^T + E0 (:func:`gsq_recon_loss_grad_offset`): for O,
+E0 = (ao_q - ao_fp) W_o^T; for down, E0 = (act_q - act_fp) W_down^T +
+(h_q - h_fp), where _q are the block's activations with the quantized earlier
+stages and _fp those of the full-precision block. ``objective="layer"`` fits
+every layer to its own output.
 """
 
 from __future__ import annotations
@@ -28,8 +38,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (GsqLion, GsqLayer, DTYPE_BF16, gsq_matmul_nt_bf16, gsq_rmsnorm_bf16,
-               gsq_softmax_causal_bf16, gsq_silu_mul_bf16, gsq_add_bf16, gsq_dequant_bf16,
-               gsq_transpose_tokens)
+               gsq_softmax_causal_bf16, gsq_silu_mul_bf16, gsq_add_bf16, gsq_sub_bf16,
+               gsq_dequant_bf16, gsq_transpose_tokens)
 from .solver import LayerSolver
 
 PROJECTIONS = ("q", "k", "v", "o", "gate", "up", "down")
@@ -123,13 +133,38 @@ def recon_form(recon: str, cols: int, tokens: int) -> str:
     return recon
 
 
+def offset_T(W: torch.Tensor, x_q: torch.Tensor, x_fp: torch.Tensor,
+             resid_q: torch.Tensor | None = None, resid_fp: torch.Tensor | None = None):
+    """E0^T = W (x_q - x_fp)^T (+ (resid_q - resid_fp)^T), [out][tokens] bf16:
+    the offset that makes a layer with input x_q fit the output x_fp W^T
+    (+ resid_fp - resid_q) of the full-precision block."""
+    n, k = x_q.shape
+    out = W.shape[0]
+    dev = x_q.device
+    d = torch.empty_like(x_q)
+    gsq_sub_bf16(n * k, x_q, x_fp, d)
+    E = _bf16((out, n), dev)
+    gsq_matmul_nt_bf16(out, n, k, W, k, d, k, E, n)
+    if resid_q is not None:
+        dr = torch.empty_like(resid_q)
+        gsq_sub_bf16(n * out, resid_q, resid_fp, dr)
+        drT = _bf16((out * n,), dev)
+        gsq_transpose_tokens(1, [0, n], out, dr, drT)
+        E2 = _bf16((out, n), dev)
+        gsq_add_bf16(out * n, E, drT, E2)
+        E = E2
+    return E
+
+
 def _quantize(W: torch.Tensor, X: torch.Tensor, grid: int, steps: int, lion: GsqLion,
-              tau0: float, tau1: float, init: str, seed: int, stream_id: int, recon: str):
+              tau0: float, tau1: float, init: str, seed: int, stream_id: int, recon: str,
+              E0T: torch.Tensor | None = None):
     """One layer's annealed solve; returns the hard weights (bf16), the last
-    relaxed loss and the reconstruction form used."""
-    form = recon_form(recon, W.shape[1], X.shape[0])
+    relaxed loss and the reconstruction form used. With an offset E0T the
+    direct form is used (the Gram form would need X^T E0 as well)."""
+    form = "direct+offset" if E0T is not None else recon_form(recon, W.shape[1], X.shape[0])
     sol = LayerSolver(W, X, grid, seed=seed, stream_id=stream_id, lion=lion, init=init,
-                      recon=form)
+                      recon="direct" if E0T is not None else form, offset_T=E0T)
     losses, (codes, _, s16) = sol.solve(steps, tau0, tau1, log_every=steps)
     Wq = torch.empty_like(W)
     layer = GsqLayer.make(grid, W.shape[0], W.shape[1], DTYPE_BF16)
@@ -139,16 +174,22 @@ def _quantize(W: torch.Tensor, X: torch.Tensor, grid: int, steps: int, lion: Gsq
 
 def staged_quantize(cfg: BlockConfig, w: dict, x: torch.Tensor, grid: int, steps: int,
                     lion: GsqLion | None = None, tau0: float = 1.0, tau1: float = 0.05,
-                    init: str = "rtn", seed: int = 0, recon: str = "direct"):
+                    init: str = "rtn", seed: int = 0, recon: str = "direct",
+                    objective: str = "block"):
     """The staged schedule. Returns ``(wq, info)``: the weights with every
     projection replaced by its hard quantized version, and per stage the wall
-    time, the calibration inputs used, the last relaxed loss and each layer's
+    time, the calibration inputs used, the last relaxed loss, each layer's
     reconstruction form (``recon``: "direct", "gram" or "auto", see
-    :func:`recon_form`)."""
+    :func:`recon_form`; "direct+offset" for a layer fitted to a
+    full-precision target) and, with ``objective="block"``, the offsets used
+    (``offset_T``: O and down)."""
     recon_form(recon, 1, 1)   # reject an unknown form before any work
+    if objective not in ("block", "layer"):
+        raise ValueError("objective must be 'block' or 'layer'")
     lion = lion or GsqLion.make()
     wq = dict(w)
     info = {}
+    fp = forward(cfg, w, x) if objective == "block" else None
 
     def stage(name, fn):
         torch.cuda.synchronize()
@@ -168,18 +209,29 @@ def staged_quantize(cfg: BlockConfig, w: dict, x: torch.Tensor, grid: int, steps
         xa = forward(cfg, wq, x)["x_attn"]
         wq["v"], lv, fv = _quantize(w["v"], xa, grid, steps, lion, tau0, tau1, init, seed, 1, recon)
         xo = forward(cfg, wq, x)["x_o"]
-        wq["o"], lo, fo = _quantize(w["o"], xo, grid, steps, lion, tau0, tau1, init, seed, 2, recon)
-        return {"x": xo, "loss": lv + lo, "recon": {"v": fv, "o": fo}}
+        e0 = offset_T(w["o"], xo, fp["x_o"]) if fp is not None else None
+        wq["o"], lo, fo = _quantize(w["o"], xo, grid, steps, lion, tau0, tau1, init, seed, 2, recon,
+                                    e0)
+        out = {"x": xo, "loss": lv + lo, "recon": {"v": fv, "o": fo}}
+        if e0 is not None:
+            out["offset_T"] = e0
+        return out
 
     def s3():
         xm = forward(cfg, wq, x)["x_mlp"]
         gu = torch.cat([w["gate"], w["up"]], dim=0)
         hgu, lgu, fgu = _quantize(gu, xm, grid, steps, lion, tau0, tau1, init, seed, 3, recon)
         wq["gate"], wq["up"] = hgu[:cfg.mlp].contiguous(), hgu[cfg.mlp:].contiguous()
-        xd = forward(cfg, wq, x)["x_down"]
+        fq = forward(cfg, wq, x)
+        xd = fq["x_down"]
+        e0 = (offset_T(w["down"], xd, fp["x_down"], fq["h"], fp["h"]) if fp is not None
+              else None)
         wq["down"], ld, fd = _quantize(w["down"], xd, grid, steps, lion, tau0, tau1, init, seed, 4,
-                                       recon)
-        return {"x": xd, "loss": lgu + ld, "recon": {"gate_up": fgu, "down": fd}}
+                                       recon, e0)
+        out = {"x": xd, "loss": lgu + ld, "recon": {"gate_up": fgu, "down": fd}}
+        if e0 is not None:
+            out["offset_T"] = e0
+        return out
 
     stage("q_k", s1)
     stage("v_o", s2)

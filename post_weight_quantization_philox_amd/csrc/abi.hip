@@ -258,6 +258,16 @@ gsq_status gsq_add_bf16(int64_t n, const uint16_t* a, const uint16_t* b, uint16_
     return hip_status(gsq::launch_add(n, a, b, out, static_cast<hipStream_t>(stream)));
 }
 
+gsq_status gsq_sub_bf16(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
+                        void* stream) {
+    if (n < 0 || n > kMaxCoords) return GSQ_ERR_SHAPE;
+    if (n == 0) return GSQ_OK;
+    GSQ_TRY(need(a));
+    GSQ_TRY(need(b));
+    GSQ_TRY(need(out));
+    return hip_status(gsq::launch_sub(n, a, b, out, static_cast<hipStream_t>(stream)));
+}
+
 gsq_status gsq_dequant_bf16(const gsq_layer* layer, const uint8_t* codes,
                             const uint16_t* scales_f16, uint16_t* W, void* stream) {
     LayerDesc d;
@@ -341,6 +351,96 @@ gsq_status gsq_recon_loss_grad_noalloc(int32_t n_experts, const int64_t* tok_off
     return hip_status(gsq::launch_recon(n_experts, tok_offsets, rows_per_expert, cols, X, XT,
                                         dW_bf16, partials, RT, G, loss,
                                         static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_recon_residual(int32_t n_experts, const int64_t* tok_offsets,
+                              int64_t rows_per_expert, int64_t cols, const uint16_t* X,
+                              const uint16_t* dW_bf16, void* workspace, size_t workspace_bytes,
+                              uint16_t* RT, void* stream) {
+    GSQ_TRY(check_offsets(n_experts, tok_offsets, rows_per_expert, cols));
+    if (tok_offsets[n_experts] > 0) {
+        GSQ_TRY(need(X));
+        GSQ_TRY(need(RT));
+    }
+    GSQ_TRY(need(dW_bf16));
+    GSQ_TRY(need(workspace));
+    if (workspace_bytes < gsq_recon_workspace_bytes(n_experts, tok_offsets, rows_per_expert, cols))
+        return GSQ_ERR_SHAPE;
+    size_t n_partials = 0;
+    return hip_status(gsq::launch_recon_gemm1(n_experts, tok_offsets, rows_per_expert, cols, X,
+                                              dW_bf16, static_cast<float*>(workspace), RT,
+                                              &n_partials, static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_recon_bwd_lion_fwd(const gsq_layer* layer, int32_t n_experts,
+                                  const int64_t* tok_offsets, const uint16_t* XT,
+                                  const uint16_t* RT, const void* workspace,
+                                  size_t workspace_bytes, double* loss, float* logits, float* mom,
+                                  float* scales, float* scale_mom, const uint8_t* init_codes,
+                                  const void* W, uint32_t step, float tau, float noise_scale,
+                                  const gsq_lion* lion, int32_t with_next, uint32_t next_step,
+                                  float next_tau, uint16_t* dW_bf16, void* stream) {
+    LayerDesc d;
+    GSQ_TRY(check_layer(layer, &d));
+    if (n_experts < 1 || layer->rows % n_experts != 0) return GSQ_ERR_SHAPE;
+    const int64_t rpe = layer->rows / n_experts;
+    GSQ_TRY(check_offsets(n_experts, tok_offsets, rpe, layer->cols));
+    if (tok_offsets[n_experts] > INT32_MAX) return GSQ_ERR_SHAPE;
+    if (tok_offsets[n_experts] > 0) {
+        GSQ_TRY(need(XT));
+        GSQ_TRY(need(RT));
+    }
+    GSQ_TRY(need(workspace));
+    GSQ_TRY(need(loss));
+    GSQ_TRY(need(logits));
+    GSQ_TRY(need(mom));
+    GSQ_TRY(need(scales));
+    GSQ_TRY(need(scale_mom));
+    if (with_next != 0 && with_next != 1) return GSQ_ERR_PARAM;
+    if (with_next) {
+        GSQ_TRY(need(W));
+        GSQ_TRY(need(dW_bf16));
+    }
+    if (d.grid == GSQ_GRID_INT3_LOCAL) {
+        if (init_codes == nullptr) return GSQ_ERR_GRID;
+        GSQ_TRY(need(init_codes));
+    }
+    if (lion == nullptr) return GSQ_ERR_NULL;
+    if (workspace_bytes < gsq_recon_workspace_bytes(n_experts, tok_offsets, rpe, layer->cols))
+        return GSQ_ERR_SHAPE;
+    gsq::TauK tk, tk_next = {};
+    GSQ_TRY(check_tau(tau, noise_scale, &tk));
+    if (with_next) GSQ_TRY(check_tau(next_tau, noise_scale, &tk_next));
+    gsq::LionK lkl, lks;
+    GSQ_TRY(lion_consts(lion->lr_logit, lion, &lkl));
+    GSQ_TRY(lion_consts(lion->lr_scale, lion, &lks));
+    const size_t n_partials = gsq::recon_partials(n_experts, tok_offsets, rpe);
+    return hip_status(gsq::launch_recon_relax(
+        d, n_experts, tok_offsets, rpe, XT, RT, static_cast<const float*>(workspace), n_partials,
+        loss, logits, mom, scales, scale_mom, init_codes, step, tk, lkl, lks, W, next_step,
+        tk_next, with_next ? dW_bf16 : nullptr, static_cast<hipStream_t>(stream)));
+}
+
+gsq_status gsq_recon_loss_grad_offset(int64_t rows, int64_t cols, int64_t tokens,
+                                     const uint16_t* X, const uint16_t* XT,
+                                     const uint16_t* dW_bf16, const uint16_t* E0T,
+                                     void* workspace, size_t workspace_bytes, uint16_t* RT,
+                                     float* G, double* loss, void* stream) {
+    if (tokens <= 0) return GSQ_ERR_SHAPE;
+    const int64_t offs[2] = {0, tokens};
+    GSQ_TRY(check_offsets(1, offs, rows, cols));
+    GSQ_TRY(need(X));
+    GSQ_TRY(need(XT));
+    GSQ_TRY(need(dW_bf16));
+    GSQ_TRY(need(E0T));
+    GSQ_TRY(need(workspace));
+    GSQ_TRY(need(RT));
+    GSQ_TRY(need(G));
+    GSQ_TRY(need(loss));
+    if (workspace_bytes < gsq_recon_workspace_bytes(1, offs, rows, cols)) return GSQ_ERR_SHAPE;
+    return hip_status(gsq::launch_recon_offset(rows, cols, tokens, X, XT, dW_bf16, E0T,
+                                               static_cast<float*>(workspace), RT, G, loss,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 gsq_status gsq_transpose_tokens(int32_t n_experts, const int64_t* tok_offsets, int64_t cols,

@@ -85,12 +85,14 @@ __global__ __launch_bounds__(kT) void silu_mul_kernel(const uint16_t* __restrict
     act[i] = to_bf16(g / (1.0f + expf(-g)) * ld_bf16(up, i));
 }
 
+// out = a + b (SUB: a - b), one fp32 operation rounded to bf16.
+template <bool SUB>
 __global__ __launch_bounds__(kT) void add_kernel(const uint16_t* __restrict__ a,
                                                  const uint16_t* __restrict__ b, int64_t n,
                                                  uint16_t* __restrict__ out) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * kT + threadIdx.x;
     if (i >= n) return;
-    out[i] = to_bf16(ld_bf16(a, i) + ld_bf16(b, i));
+    out[i] = to_bf16(SUB ? ld_bf16(a, i) - ld_bf16(b, i) : ld_bf16(a, i) + ld_bf16(b, i));
 }
 
 // Hard weights s * v(code) in bf16 from stored codes and fp16 scales.
@@ -135,7 +137,13 @@ hipError_t launch_silu_mul(int64_t n, const uint16_t* gate, const uint16_t* up, 
 
 hipError_t launch_add(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
                       hipStream_t st) {
-    hipLaunchKernelGGL(add_kernel, dim3(nblk(n)), dim3(kT), 0, st, a, b, n, out);
+    hipLaunchKernelGGL(add_kernel<false>, dim3(nblk(n)), dim3(kT), 0, st, a, b, n, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_sub(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
+                      hipStream_t st) {
+    hipLaunchKernelGGL(add_kernel<true>, dim3(nblk(n)), dim3(kT), 0, st, a, b, n, out);
     return hipGetLastError();
 }
 

@@ -48,8 +48,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Epilogues: bf16 output plus the tile's sum of squares (GEMM1); fp32 output
 // times alpha (GEMM2); plain bf16 output (the Gram matrix); fp32 output times
 // alpha plus the tile's sum of D[i][j] * C[i][j] before scaling (the Gram-form
-// step, where D = dW and C = dW H, so the sum is the loss).
-enum { EPI_BF16_LOSS = 0, EPI_F32_SCALED = 1, EPI_BF16 = 2, EPI_F32_GRAM = 3 };
+// step, where D = dW and C = dW H, so the sum is the loss); and GEMM1 with a
+// fixed bf16 offset D added to C before the square and the rounding (the
+// residual R^T = dW X^T + E0^T of a layer fitted to a target downstream).
+enum { EPI_BF16_LOSS = 0, EPI_F32_SCALED = 1, EPI_BF16 = 2, EPI_F32_GRAM = 3,
+       EPI_BF16_LOSS_OFF = 4 };
 
 struct GemmArgs {
     const uint16_t* A;
@@ -60,8 +63,8 @@ struct GemmArgs {
     int tiles_i, tiles_j;
     void* C;
     float alpha;
-    float* partials;   // EPI_BF16_LOSS, EPI_F32_GRAM: one float per workgroup
-    const uint16_t* D; // EPI_F32_GRAM: bf16 [I][ldd] paired with the output
+    float* partials;   // EPI_BF16_LOSS(_OFF), EPI_F32_GRAM: one float per workgroup
+    const uint16_t* D; // EPI_F32_GRAM, EPI_BF16_LOSS_OFF: bf16 [I][ldd] paired with the output
     int64_t ldd;
     // Optional: workgroup 0 first sums fin_n loss partials of an earlier
     // launch into *fin_loss (the same order as loss_finalize_kernel), which
@@ -418,19 +421,27 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
             }
         }
         __syncthreads();
-        if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_BF16) {
+        if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_BF16 || EPI == EPI_BF16_LOSS_OFF) {
             // 16 lanes per 128-value row: 8 values -> one 16-byte bf16 store.
             constexpr int LPR = WN / 8;   // lanes per row
 #pragma unroll
             for (int t = 0; t < 32 * LPR / 64; ++t) {
                 const int c = lane + 64 * t;
                 const int row = c / LPR, col = (c % LPR) * 8;
-                const float4 v0 = *reinterpret_cast<const float4*>(slab + row * kSlab + col);
-                const float4 v1 = *reinterpret_cast<const float4*>(slab + row * kSlab + col + 4);
+                float4 v0 = *reinterpret_cast<const float4*>(slab + row * kSlab + col);
+                float4 v1 = *reinterpret_cast<const float4*>(slab + row * kSlab + col + 4);
                 const int grow = grow0 + a * 32 + row, gcol = gcol0 + col;
                 if (grow < g.I && gcol < g.J) {
                     const int64_t off = static_cast<int64_t>(grow) * g.ldc + gcol;
-                    if constexpr (EPI == EPI_BF16_LOSS) {
+                    if constexpr (EPI == EPI_BF16_LOSS_OFF) {
+                        const uint4 e = *reinterpret_cast<const uint4*>(
+                            g.D + static_cast<int64_t>(grow) * g.ldd + gcol);
+                        v0.x += bf16_lo(e.x); v0.y += bf16_hi(e.x);
+                        v0.z += bf16_lo(e.y); v0.w += bf16_hi(e.y);
+                        v1.x += bf16_lo(e.z); v1.y += bf16_hi(e.z);
+                        v1.z += bf16_lo(e.w); v1.w += bf16_hi(e.w);
+                    }
+                    if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_BF16_LOSS_OFF) {
                         lsum = __builtin_fmaf(v0.x, v0.x, lsum); lsum = __builtin_fmaf(v0.y, v0.y, lsum);
                         lsum = __builtin_fmaf(v0.z, v0.z, lsum); lsum = __builtin_fmaf(v0.w, v0.w, lsum);
                         lsum = __builtin_fmaf(v1.x, v1.x, lsum); lsum = __builtin_fmaf(v1.y, v1.y, lsum);
@@ -471,7 +482,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
         }
         __syncthreads();
     }
-    if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_F32_GRAM) {
+    if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_F32_GRAM || EPI == EPI_BF16_LOSS_OFF) {
         // Fixed-order reduction: wave butterfly, then waves 0..3 in order.
         __shared__ float red[NT / 64];
 #pragma unroll
@@ -527,7 +538,7 @@ void launch_part(GemmArgs g, int r0, int c0, int I, int J, float* partials, hipS
     g.I = I; g.J = J;
     g.a_bytes = static_cast<int>(static_cast<int64_t>(I) * g.lda * 2);
     g.b_bytes = static_cast<int>(static_cast<int64_t>(J) * g.ldb * 2);
-    constexpr int esz = (EPI == EPI_BF16_LOSS || EPI == EPI_BF16) ? 2 : 4;
+    constexpr int esz = (EPI == EPI_BF16_LOSS || EPI == EPI_BF16 || EPI == EPI_BF16_LOSS_OFF) ? 2 : 4;
     g.C = static_cast<char*>(g.C) + (static_cast<int64_t>(r0) * g.ldc + c0) * esz;
     g.partials = partials;
     g.tiles_i = cdiv(I, BM); g.tiles_j = cdiv(J, TBN);
@@ -738,6 +749,67 @@ hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t r
     hipLaunchKernelGGL(loss_finalize_kernel, dim3(1), dim3(256), 0, st, partials,
                        static_cast<int>(slot), loss);
     return hipGetLastError();
+}
+
+hipError_t launch_recon_gemm1(int32_t n_experts, const int64_t* tok_offsets, int64_t rows_per_expert,
+                              int64_t cols, const uint16_t* X, const uint16_t* dW, float* partials,
+                              uint16_t* RT, size_t* n_partials, hipStream_t st) {
+    *n_partials = 0;
+    if (n_experts == 1) {
+        const int64_t ne = tok_offsets[1];
+        if (ne == 0) return hipSuccess;
+        *n_partials = static_cast<size_t>(product_workgroups(static_cast<int>(rows_per_expert),
+                                                            static_cast<int>(ne)));
+        return run_gemm<EPI_BF16_LOSS>(dW, cols, X, cols, static_cast<int>(rows_per_expert),
+                                       static_cast<int>(ne), static_cast<int>(cols), RT, ne, 1.0f,
+                                       partials, st);
+    }
+    for (int e0 = 0; e0 < n_experts; e0 += kMaxGroups) {
+        const int e1 = e0 + kMaxGroups < n_experts ? e0 + kMaxGroups : n_experts;
+        ExpertBatch eb{};
+        eb.n = e1 - e0;
+        eb.stage = 0;
+        eb.rpe = static_cast<int>(rows_per_expert);
+        eb.cols = static_cast<int>(cols);
+        eb.expert0 = e0;
+        eb.dW = dW; eb.X = X; eb.RT = RT;
+        const int64_t lim = static_cast<int64_t>(kOob) - 2 * cols - 2 * tok_offsets[e1];
+        if (rows_per_expert * cols * 2 > lim) return hipErrorInvalidValue;
+        const int ti = cdiv(rows_per_expert, BM);
+        int wg = 0;
+        for (int e = 0; e <= eb.n; ++e) eb.tok[e] = static_cast<int>(tok_offsets[e0 + e]);
+        for (int e = 0; e < eb.n; ++e) {
+            const int64_t ne = eb.tok[e + 1] - eb.tok[e];
+            if (ne * cols * 2 > lim) return hipErrorInvalidValue;
+            eb.wg0[e] = wg;
+            wg += ti * cdiv(ne, BN);
+        }
+        eb.wg0[eb.n] = wg;
+        if (wg > 0) {
+            GemmArgs g{};
+            g.alpha = 1.0f;
+            g.partials = partials + *n_partials;
+            hipLaunchKernelGGL((gemm_nt_kernel<EPI_BF16_LOSS, true, BN>), dim3(wg), dim3(NT), 0, st, g, eb);
+            const hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+        }
+        *n_partials += static_cast<size_t>(wg);
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_recon_offset(int64_t rows, int64_t cols, int64_t tokens, const uint16_t* X,
+                               const uint16_t* XT, const uint16_t* dW, const uint16_t* E0T,
+                               float* partials, uint16_t* RT, float* G, double* loss,
+                               hipStream_t st) {
+    hipError_t err = run_gemm<EPI_BF16_LOSS_OFF>(dW, cols, X, cols, static_cast<int>(rows),
+                                                 static_cast<int>(tokens), static_cast<int>(cols), RT,
+                                                 tokens, 1.0f, partials, st, E0T, tokens);
+    if (err != hipSuccess) return err;
+    const int slot = product_workgroups(static_cast<int>(rows), static_cast<int>(tokens));
+    return run_gemm<EPI_F32_SCALED>(RT, tokens, XT, tokens, static_cast<int>(rows),
+                                    static_cast<int>(cols), static_cast<int>(tokens), G, cols, 2.0f,
+                                    nullptr, st, nullptr, 0, partials, slot, loss);
 }
 
 size_t gram_partials(int64_t rows, int64_t cols) {

@@ -46,6 +46,28 @@ size_t recon_partials(int32_t n_experts, const int64_t* tok_offsets, int64_t row
 hipError_t launch_recon(int32_t n_experts, const int64_t* tok_offsets, int64_t rows_per_expert,
                         int64_t cols, const uint16_t* X, const uint16_t* XT, const uint16_t* dW,
                         float* partials, uint16_t* RT, float* G, double* loss, hipStream_t st);
+// The first product alone (R^T and the loss partials, in the same launches
+// and partial order as launch_recon); *n_partials receives the count.
+hipError_t launch_recon_gemm1(int32_t n_experts, const int64_t* tok_offsets, int64_t rows_per_expert,
+                              int64_t cols, const uint16_t* X, const uint16_t* dW, float* partials,
+                              uint16_t* RT, size_t* n_partials, hipStream_t st);
+// The second product fused with backward + Lion (and the next forward when
+// dW_next is given): G = 2 R^T X is formed tile by tile on the matrix cores
+// and consumed in registers, never stored. The first launch also sums
+// n_partials loss partials into *loss (fused.hip).
+hipError_t launch_recon_relax(const LayerDesc& d, int32_t n_experts, const int64_t* tok_offsets,
+                              int64_t rows_per_expert, const uint16_t* XT, const uint16_t* RT,
+                              const float* partials, size_t n_partials, double* loss,
+                              float* logits, float* mom, float* scales, float* scale_mom,
+                              const uint8_t* codes, uint32_t step, TauK tk, LionK lkl, LionK lks,
+                              const void* W, uint32_t next_step, TauK tk_next, uint16_t* dW_next,
+                              hipStream_t st);
+// One dense layer's objective with a fixed offset on the residual:
+// R^T = dW X^T + E0T (bf16 [rows][tokens]), loss = sum R^2, G = 2 R^T X.
+hipError_t launch_recon_offset(int64_t rows, int64_t cols, int64_t tokens, const uint16_t* X,
+                               const uint16_t* XT, const uint16_t* dW, const uint16_t* E0T,
+                               float* partials, uint16_t* RT, float* G, double* loss,
+                               hipStream_t st);
 size_t gram_partials(int64_t rows, int64_t cols);
 hipError_t launch_gram(int64_t tokens, int64_t cols, const uint16_t* XT, uint16_t* H,
                        hipStream_t st);
@@ -83,6 +105,8 @@ hipError_t launch_softmax_causal(int64_t n, const uint16_t* S, float scale, uint
 hipError_t launch_silu_mul(int64_t n, const uint16_t* gate, const uint16_t* up, uint16_t* act,
                            hipStream_t st);
 hipError_t launch_add(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
+                      hipStream_t st);
+hipError_t launch_sub(int64_t n, const uint16_t* a, const uint16_t* b, uint16_t* out,
                       hipStream_t st);
 hipError_t launch_dequant(const LayerDesc& d, const uint8_t* codes, const uint16_t* s16,
                           uint16_t* W, hipStream_t st);

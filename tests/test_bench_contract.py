@@ -40,24 +40,35 @@ def test_json_line_contract():
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
     r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3",
-                        "--warmup", "1", "--cpu-rows", "64"],
-                       capture_output=True, text=True, timeout=600, cwd=ROOT)
+                        "--warmup", "1", "--cpu-experts", "1"],
+                       capture_output=True, text=True, timeout=900, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.strip()]
     assert len(lines) == 1
     d = json.loads(lines[0])
     for k, t in [("metric", str), ("value", float), ("unit", str), ("n_gpus", int), ("steps", int),
                  ("warmup", int), ("ms_per_step", float), ("higher_is_better", bool),
-                 ("scaling", str), ("dtype", str), ("data", str), ("config", dict),
+                 ("dtype", str), ("data", str), ("config", dict),
                  ("roofline", dict), ("cpu_baseline", dict)]:
         assert isinstance(d[k], t), k
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["vs_baseline"] is None
     assert "workload" in d["config"]
+    # the headline is the largest workload that fits one GPU: the 64-expert batch
+    assert d["config"]["name"] == "moe64x2048x7168_int2" and d["config"]["experts"] == 64
+    assert set(d["variants"]) == {"qproj4096_int2", "downproj4096x14336_ternary",
+                                  "gateproj28672x8192_int3local"}
     roof = d["roofline"]
     assert roof["bound"] in ("hbm", "mfma", "alu")
     assert roof["unit"] in ("GB/s", "TFLOP/s")
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-9
     assert roof["traffic"] is None or roof["traffic"] > 0
+    # algorithmic bytes (forward + backward + Lion of one step) over the
+    # launch time, and beside them the bytes the fused pass moves
+    coords = d["config"]["rows"] * d["config"]["cols"]
+    assert roof["algorithmic_bytes_per_launch"] == roof["algorithmic_bytes_per_coord"] * coords
+    assert abs(roof["achieved"] - roof["algorithmic_bytes_per_launch"] / roof["launch_ms"] / 1e6) \
+        <= 1e-9 * roof["achieved"]
+    assert roof["achieved_moved"] <= roof["achieved"]
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
     assert abs(d["value"] * d["ms_per_step"] / 1e3 - d["config"]["rows"] * d["config"]["cols"]) \

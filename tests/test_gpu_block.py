@@ -160,21 +160,27 @@ def test_block_forward_matches_mirror(dev):
         assert e <= 4 * 2.0 ** -8, k
 
 
-@pytest.mark.parametrize("recon", ["direct", "gram"])
-def test_staged_schedule(dev, recon):
-    """The staged schedule on a small block, with every layer on the direct
-    products or on the Gram form: each stage's calibration inputs equal the
-    oracle's mirror forward with the GPU's quantized weights of the earlier
-    stages, every projection ends quantized (dequantised values on the grid),
-    and the quantized block's output error is reported against the
-    round-to-nearest block."""
+@pytest.mark.parametrize("recon,objective", [("direct", "block"), ("gram", "block"),
+                                             ("direct", "layer"), ("gram", "layer")])
+def test_staged_schedule(dev, recon, objective):
+    """The staged schedule on a small block, with the layers on the direct
+    products or on the Gram form, each fitted to its own output (``layer``)
+    or, for the output and down projections, to the full-precision block
+    (``block``): each stage's calibration inputs equal the oracle's mirror
+    forward with the GPU's quantized weights of the earlier stages, every
+    projection ends quantized (dequantised values on the grid), the offsets
+    equal the oracle's, and the quantized block's output error is reported
+    against the round-to-nearest block."""
     import torch
     import post_weight_quantization_philox_amd as g
     from post_weight_quantization_philox_amd.block import forward, staged_quantize
     cfg, w_np, w_dev, x, xd = _small_block(dev, seed=4)
     wq, info = staged_quantize(cfg, w_dev, xd, oracle.GRID_INT2, 24,
-                               g.GsqLion.make(lr_logit=5e-2, lr_scale=1e-6), recon=recon)
-    assert all(f == recon for v in info.values() for f in v["recon"].values())
+                               g.GsqLion.make(lr_logit=5e-2, lr_scale=1e-6), recon=recon,
+                               objective=objective)
+    forms = {k: f for v in info.values() for k, f in v["recon"].items()}
+    fitted = {"o", "down"} if objective == "block" else set()
+    assert all(f == ("direct+offset" if k in fitted else recon) for k, f in forms.items())
     wq_np = dict(w_np)
     for name in ("q", "k", "v", "o", "gate", "up", "down"):
         wq_np[name] = bf16_values(wq[name]).astype(np.float64)
@@ -198,6 +204,33 @@ def test_staged_schedule(dev, recon):
     full = ob.block_forward(x, w_np, SMALL)["out"]
     e_gsq = _nrm(ob.block_forward(x, wq_np, SMALL)["out"], full)
     e_rtn = _nrm(ob.block_forward(x, w_rtn, SMALL)["out"], full)
-    report(f"staged schedule ({recon})", x_down_vs_mirror=e_in, x_o_vs_mirror=e_xo, out_err_gsq=e_gsq,
-           out_err_rtn=e_rtn, **{f"{k}_s": v["seconds"] for k, v in info.items()})
+    extra = {}
+    if objective == "block":
+        # The offsets against the oracle's, each from the mirror forward with
+        # the GPU's quantized earlier stages and the full-precision block.
+        fp = ob.block_forward_mirror(x, w_np, SMALL)
+        fo = ob.block_forward_mirror(x, dict(wq_np, o=w_np["o"], gate=w_np["gate"],
+                                             up=w_np["up"], down=w_np["down"]), SMALL)
+        e0o = ob.stage_offset_T(w_np["o"], fo["x_o"], fp["x_o"], mirror=True)
+        got_o = bf16_values(info["v_o"]["offset_T"]).astype(np.float64)
+        fd = ob.block_forward_mirror(x, dict(wq_np, down=w_np["down"]), SMALL)
+        e0d = ob.stage_offset_T(w_np["down"], fd["x_down"], fp["x_down"], fd["h"], fp["h"],
+                                mirror=True)
+        got_d = bf16_values(info["mlp"]["offset_T"]).astype(np.float64)
+        extra = {"offset_o_vs_mirror": _nrm(got_o, e0o), "offset_down_vs_mirror": _nrm(got_d, e0d)}
+        # The down stage's objective at the hard result is the block output
+        # error: act_q (W_q - W)^T + E0 equals out_q - out_fp.
+        act = bf16_values(info["mlp"]["x"]).astype(np.float64)
+        R = act @ (wq_np["down"] - w_np["down"]).T + got_d.T
+        want = ob.block_forward_mirror(x, wq_np, SMALL)["out"] - fp["out"]
+        extra["down_objective_vs_block_error"] = _nrm(R, want)
+        # Offsets are differences of near-equal activations, rounded once
+        # more than the activations themselves, so the bar is relative to
+        # their own (small) norm: 8 bf16 ulps.
+        assert extra["offset_o_vs_mirror"] <= 8 * 2.0 ** -8
+        assert extra["offset_down_vs_mirror"] <= 8 * 2.0 ** -8
+        assert extra["down_objective_vs_block_error"] <= 8 * 2.0 ** -8
+    report(f"staged schedule ({recon}, {objective})", x_down_vs_mirror=e_in, x_o_vs_mirror=e_xo,
+           out_err_gsq=e_gsq, out_err_rtn=e_rtn, **extra,
+           **{f"{k}_s": v["seconds"] for k, v in info.items()})
     assert e_in <= 4 * 2.0 ** -8 and e_xo <= 4 * 2.0 ** -8

@@ -303,7 +303,7 @@ def test_beyond_32bit_offsets():
 
 
 def _trajectory_rows(sol, d, rows, x_of_row, gpu_row_loss, T, lr_logit, lr_scale, sid,
-                     init_logit, label, t0):
+                     init_logit, label, t0, loss_bar=2e-3, groups=None):
     """Run ``T`` annealed steps of ``sol`` (objective, then fused backward +
     Lion + next forward, at the solver's own temperatures) and compare the
     sampled ``rows`` with the oracle's step loop at the oracle's temperatures,
@@ -375,6 +375,12 @@ def _trajectory_rows(sol, d, rows, x_of_row, gpu_row_loss, T, lr_logit, lr_scale
     same_logits = float(np.mean(f32(sol.logits[:, rows]) == np.stack(rows_state, axis=1)))
     agree = float(np.mean(codes == c_ref))
     moved = float(np.mean(c_ref != c0))
+    for name, idx in (groups or {}).items():
+        ge, gr = gpu[:, idx].sum(axis=1), ref[:, idx].sum(axis=1)
+        report(f"  {name}", max_rel_loss=float((np.abs(ge - gr) / gr).max()),
+               max_rel_single_row=float(rel_rows[:, idx].max()),
+               step_of_max=int(np.argmax(np.abs(ge - gr) / gr)))
+    print("[parity]   per-step rel of the total: " + " ".join(f"{v:.1e}" for v in rel), flush=True)
     report(f"{label} trajectory on sampled rows", max_rel_loss=float(rel.max()),
            max_rel_single_row=float(rel_rows.max()), logits_identical=same_logits,
            code_agreement=agree, codes_moved_from_init=moved, max_logit_flips=float(flips.max()),
@@ -382,7 +388,7 @@ def _trajectory_rows(sol, d, rows, x_of_row, gpu_row_loss, T, lr_logit, lr_scale
     # Every step matches the oracle up to sign decisions on c within rounding
     # of zero, which are counted and must stay below 1e-4 of the parameters.
     assert flips.max() <= 1e-4 and sflips.max() <= 1e-4
-    assert rel.max() <= 2e-3
+    assert rel.max() <= loss_bar
     # Over the free-running steps those decisions compound (each leaves a
     # logit 2 lr away from the oracle's, and later steps follow from there),
     # most on the ternary layer, whose logits start near the threshold where
@@ -456,9 +462,12 @@ def test_fullsize_expert_batch_trajectory_sampled_rows():
                       tok_offsets=offs, rows_per_expert=rpe, seed=0, stream_id=sid,
                       lion=g.GsqLion.make(lr_logit=lr_logit, lr_scale=lr_scale))
     poffs = [int(o) for o in sol.tok_offsets]          # padded to 64 on the device
+    # 48 rows per expert: a few hundred tokens make each row's loss move more
+    # with every legitimate sign difference than a 4096-token row's, so the
+    # free-running total needs more rows to stand for the experts' loss.
     rng = np.random.default_rng(1)
     rows = sorted({e * rpe + int(i) for e in experts
-                   for i in [0, 1, rpe // 2, rpe - 1, *rng.integers(0, rpe, 2)]})
+                   for i in [0, 1, rpe // 2, rpe - 1, *rng.choice(rpe, 44, replace=False)]})
     X = d["X"].astype(np.float64)
     x_blocks = {e: X[offs[e]:offs[e + 1]] for e in experts}
 
@@ -472,5 +481,7 @@ def test_fullsize_expert_batch_trajectory_sampled_rows():
             out[j] = float((rt * rt).sum())
         return out
 
+    groups = {f"expert {e} ({int(counts[e])} tokens)": [j for j, r in enumerate(rows) if r // rpe == e]
+              for e in experts}
     _trajectory_rows(sol, d, rows, lambda r: x_blocks[r // rpe], gpu_row_loss, T, lr_logit,
-                     lr_scale, sid, 2.0, name, t0)
+                     lr_scale, sid, 2.0, name, t0, groups=groups)

@@ -294,6 +294,54 @@ def test_recon_loss_grad(dev, M, N, K, offs):
 @pytest.mark.parametrize("M,N,K", [
     (512, 256, 512),                  # several tiles
     (300, 192, 384),                  # ragged rows, partial tiles
+    (4000, 5056, 128),                # R^T: column block + ragged 128-wide tail
+    (5000, 4096, 128),                # R^T: row block + ragged tail
+])
+def test_recon_loss_grad_offset(dev, M, N, K):
+    """R = X dW^T + E0 (a layer fitted to a target downstream): E0^T enters
+    the first product's epilogue, so R^T, the loss and G follow the oracle's
+    offset objective; the offset is read at the right place in split tiles."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    rng = np.random.default_rng(M + 3 * N + K)
+    dW_bits = synthetic.bf16_bits((rng.normal(0, 0.01, (M, K))).astype(np.float32))
+    X_bits = synthetic.bf16_bits(rng.normal(0, 1, (N, K)).astype(np.float32))
+    E_bits = synthetic.bf16_bits(rng.normal(0, 0.1, (M, N)).astype(np.float32))
+    dW = synthetic.bf16_to_f32(dW_bits).astype(np.float64)
+    X = synthetic.bf16_to_f32(X_bits).astype(np.float64)
+    E0T = synthetic.bf16_to_f32(E_bits).astype(np.float64)
+    tX = to_dev_bf16(X_bits, dev)
+    XT = torch.empty((N * K,), dtype=torch.bfloat16, device=dev)
+    g.gsq_transpose_tokens(1, [0, N], K, tX, XT)
+    RT = torch.full((M * N,), float("nan"), dtype=torch.bfloat16, device=dev)
+    G = torch.full((M, K), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty((g.gsq_recon_workspace_bytes(1, [0, N], M, K) // 4,), dtype=torch.float32,
+                     device=dev)
+    loss = torch.zeros((1,), dtype=torch.float64, device=dev)
+    g.gsq_recon_loss_grad_offset(M, K, N, tX, XT, to_dev_bf16(dW_bits, dev),
+                                 to_dev_bf16(E_bits, dev), ws, RT, G, loss)
+    torch.cuda.synchronize()
+    RT_ref, loss_ref, _ = oracle.recon_loss_grad_offset(X, dW, E0T)
+    rel = abs(float(loss.item()) - loss_ref) / loss_ref
+    got_rt = bf16_values(RT).astype(np.float64).reshape(M, N)
+    # fp32 dot product (worst case (K+2) 2^-24 sum|terms|), one fp32 add of
+    # the offset, one rounding to bf16 (half an ulp)
+    gam = (K + 2) * 2.0 ** -24 * (np.abs(dW) @ np.abs(X).T) + 2.0 ** -23 * np.abs(RT_ref)
+    ok_rt = np.all(np.abs(got_rt - RT_ref) <= 0.5 * bf16_ulp(RT_ref) + gam + 1e-30)
+    Ge = 2.0 * got_rt @ X
+    bound = (N + 2) * 2.0 ** -24 * (2.0 * np.abs(got_rt) @ np.abs(X))
+    Gd = f32(G).astype(np.float64)
+    nrm = np.linalg.norm(Gd - Ge) / np.linalg.norm(Ge)
+    report(f"recon offset {M}x{N}x{K}", rel_loss=rel, G_normwise=float(nrm))
+    assert rel <= 1e-5
+    assert ok_rt
+    assert np.all(np.abs(Gd - Ge) <= bound + 1e-30)
+    assert nrm <= 1e-5
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (512, 256, 512),                  # several tiles
+    (300, 192, 384),                  # ragged rows, partial tiles
     (256, 64, 640),                   # few tokens, in-features past two tiles
     (4352, 64, 4096),                 # 17x16 tiles: a row block of whole rounds + a 128-wide tail
 ])

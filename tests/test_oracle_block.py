@@ -140,3 +140,52 @@ def test_mirror_close_to_exact_forward():
         for k in KEYS:
             e = np.linalg.norm(got[k] - ref[k]) / np.linalg.norm(ref[k])
             assert 0 < e <= 2.0 ** -6, (k, e)
+
+
+def _perturbed(w, seed, scale=0.05):
+    rng = np.random.default_rng(seed)
+    return {k: (v + scale * np.abs(v).mean() * rng.normal(size=v.shape)
+                if k in ("q", "k", "v", "o", "gate", "up", "down") else v) for k, v in w.items()}
+
+
+def test_output_projection_offset_is_attention_output_error():
+    """With the offset, the output projection's objective on the quantized
+    attention output is the error of the block's residual stream after
+    attention against the full-precision block: ||h_q - h_fp||^2."""
+    cfg, w, x = _block_case(10, bf16=False)
+    wq = _perturbed(w, 11)
+    fp = ob.block_forward(x, w, cfg)
+    fq = ob.block_forward(x, dict(wq, o=w["o"]), cfg)        # q, k, v quantized
+    E0T = ob.stage_offset_T(w["o"], fq["x_o"], fp["x_o"])
+    _, loss, _ = oracle.recon_loss_grad_offset(fq["x_o"], wq["o"] - w["o"], E0T)
+    h_q = ob.block_forward(x, wq, cfg)["h"]
+    want = float(np.sum((h_q - fp["h"]) ** 2))
+    assert abs(loss - want) <= 1e-10 * want
+
+
+def test_down_projection_offset_is_block_output_error():
+    """With the offset, the down projection's objective on the quantized
+    SwiGLU activations is the block output error against the full-precision
+    block, ||out_q - out_fp||^2 (the MLP fitted on the block output)."""
+    cfg, w, x = _block_case(12, bf16=False)
+    wq = _perturbed(w, 13)
+    fp = ob.block_forward(x, w, cfg)
+    fq = ob.block_forward(x, dict(wq, down=w["down"]), cfg)
+    E0T = ob.stage_offset_T(w["down"], fq["x_down"], fp["x_down"], fq["h"], fp["h"])
+    RT, loss, _ = oracle.recon_loss_grad_offset(fq["x_down"], wq["down"] - w["down"], E0T)
+    out_q = ob.block_forward(x, wq, cfg)["out"]
+    np.testing.assert_allclose(RT.T, out_q - fp["out"], rtol=1e-9, atol=1e-12)
+    assert abs(loss - float(np.sum((out_q - fp["out"]) ** 2))) <= 1e-10 * loss
+    # without a quantized earlier stage and with dW = 0 the objective vanishes
+    E0_same = ob.stage_offset_T(w["down"], fp["x_down"], fp["x_down"], fp["h"], fp["h"])
+    assert not np.any(E0_same)
+
+
+def test_stage_offset_mirror_rounds_like_the_exact_offset():
+    cfg, w, x = _block_case(14)
+    wq = _perturbed(w, 15)
+    fp = ob.block_forward(x, w, cfg)
+    fq = ob.block_forward(x, dict(wq, down=w["down"]), cfg)
+    ex = ob.stage_offset_T(w["down"], fq["x_down"], fp["x_down"], fq["h"], fp["h"])
+    mi = ob.stage_offset_T(w["down"], fq["x_down"], fp["x_down"], fq["h"], fp["h"], mirror=True)
+    assert 0 < np.linalg.norm(mi - ex) / np.linalg.norm(ex) <= 2.0 ** -6

@@ -585,3 +585,35 @@ def test_step_on_row_blocks_equals_whole_layer_step(grid):
             np.testing.assert_array_equal(st[key], whole[key][:, r])
         for key in ("scales", "scale_mom"):
             np.testing.assert_array_equal(st[key], whole[key][r])
+
+
+def test_offset_objective():
+    """R = X dW^T + E0: the loss is ||X W_soft^T - Y||^2 for E0 = X W^T - Y
+    (computed token by token, independently), zero at the dW that makes the
+    output match, the plain objective for E0 = 0, and its gradient matches
+    central finite differences."""
+    rng = np.random.default_rng(12)
+    n, k, m = 30, 16, 5
+    X = rng.normal(size=(n, k))
+    W = rng.normal(size=(m, k)) * 0.1
+    Y = rng.normal(size=(n, m))
+    D = rng.normal(size=(m, k)) * 0.01
+    E0T = (X @ W.T - Y).T
+    RT, loss, G = oracle.recon_loss_grad_offset(X, D, E0T)
+    want = sum(float(np.dot(X[t], W[o] + D[o]) - Y[t, o]) ** 2 for t in range(n) for o in range(m))
+    assert math.isclose(loss, want, rel_tol=1e-12)
+    # the dW that reproduces Y exactly where Y is reachable: Y = X W2^T
+    W2 = rng.normal(size=(m, k)) * 0.1
+    _, l0, G0 = oracle.recon_loss_grad_offset(X, W2 - W, (X @ W.T - X @ W2.T).T)
+    assert l0 <= 1e-20 and np.abs(G0).max() <= 1e-12
+    _, lp, Gp = oracle.recon_loss_grad(X, D)
+    _, lz, Gz = oracle.recon_loss_grad_offset(X, D, np.zeros((m, n)))
+    assert lz == lp and np.array_equal(Gz, Gp)
+    h = 1e-7
+    for idx in [(0, 0), (2, 9), (4, 15)]:
+        Dp, Dm = D.copy(), D.copy()
+        Dp[idx] += h
+        Dm[idx] -= h
+        fd = (oracle.recon_loss_grad_offset(X, Dp, E0T)[1]
+              - oracle.recon_loss_grad_offset(X, Dm, E0T)[1]) / (2 * h)
+        assert abs(fd - G[idx]) <= 1e-6 * np.abs(G).max()
