@@ -127,16 +127,24 @@ def test_fullsize_sampled_parity(name):
     torch.cuda.synchronize()
     gl_rows = f32(gl[:, rows])
     gs_rows = f32(gs[rows])
+    per_coord = []
     for j, r in enumerate(rows):
         glr, gsr = oracle.relax_bwd(Gh[j:j + 1], l_ref[:, j:j + 1], s_ref[j:j + 1], grid, 0, 0, step,
                                     tau, 1.0, c_ref[j:j + 1], row0=r)
         nat = np.abs(Gh[j]) * np.repeat(s_ref[j].astype(np.float64), 128) * oracle.Q_MAX[grid] / tau
         assert np.all(np.abs(gl_rows[:, j] - glr[:, 0]) <= 1e-5 * nat[None] + 1e-30)
+        cmax = np.abs(glr[:, 0]).max(axis=0)
+        live = cmax >= 1e-3 * nat
+        per_coord.append((np.abs(gl_rows[:, j] - glr[:, 0]).max(axis=0) / np.maximum(cmax, 1e-300))[live])
         f = oracle.relax_fwd(l_ref[:, j:j + 1], s_ref[j:j + 1], W[r:r + 1], grid, 0, 0, step, tau, 1.0,
                              c_ref[j:j + 1], row0=r)
         mass = (np.abs(Gh[j]) * np.abs(f["w_hat"][0])).reshape(-1, 128).sum(1)
         gabs = np.abs(Gh[j]).reshape(-1, 128).sum(1)
         assert np.all(np.abs(gs_rows[j] - gsr[0]) <= 130 * 2.0 ** -24 * mass + 1e-5 * oracle.Q_MAX[grid] * gabs)
+    pc = np.concatenate(per_coord)
+    report(f"{name} logit gradient per coordinate (|grad| >= 1e-3 of natural scale)",
+           max_rel=float(pc.max()), p999=float(np.quantile(pc, 0.999)), median=float(np.median(pc)),
+           within_1e5=float(np.mean(pc <= 1e-5)))
     th, _ = oracle.lion(l_ref, gl_rows, np.zeros_like(l_ref), wl.lr_logit, 0.9, 0.99)
     np.testing.assert_array_equal(f32(keep[0][:, rows]).view(np.uint32), th.view(np.uint32))
     _log(f"{name}: relax_bwd_lion ok")
