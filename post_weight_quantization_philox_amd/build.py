@@ -30,6 +30,14 @@ HIPCC_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
+# Per-source flags. The products' K-loop carries 64 MFMA accumulator tuples
+# from one K-step to the next; under the default scheduler the register
+# allocator shuffles some of them between register files every step, which
+# the iterative ILP strategy avoids (every accumulator stays in its AGPRs).
+EXTRA_FLAGS = {
+    "gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
 
 def _hipcc() -> str:
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -45,7 +53,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -11,17 +11,18 @@
 // at once, so G never reaches HBM.
 //
 // Every G value is the same MFMA chain, in the same k order, as in the
-// stand-alone product (gemm.hip): v_mfma_f32_32x32x16_bf16 over 16-wide
-// slices in order, lane half h holding k = 16 s + 8 h .. + 7 of slice s. So
-// G, and everything computed from it, is bit-identical to the two-kernel
+// stand-alone product (gemm.hip): v_mfma_f32_16x16x32_bf16 over 32-wide
+// slices in order, lane quarter q holding k = 32 s + 8 q .. + 7 of slice s.
+// So G, and everything computed from it, is bit-identical to the two-kernel
 // path.
 //
 // Workgroup: 4 waves over a tile of 32 rows x 512 columns; wave w owns
-// columns 128w .. 128w+127 (one scale group per row) of all 32 rows (4 blocks
-// of 32x32, 64 accumulators per lane). Fragments come straight from global
-// memory (R^T and X^T are small next to the state and stay in the caches).
-// A wave's accumulators pass through its own LDS slab (32 x 128 fp32, rows
-// padded so the two half-waves' stores land 32 banks apart) into the relax
+// columns 128w .. 128w+127 (one scale group per row) of all 32 rows (2 x 8
+// blocks of 16x16, 64 accumulators per lane). Fragments come straight from
+// global memory (R^T and X^T are small next to the state and stay in the
+// caches). A wave's accumulators pass through its own LDS slab (32 x 128 fp32,
+// rows padded to 132 floats so the four lane quarters' stores land 16 banks
+// apart) into the relax
 // layout: per row, lane l owns columns 2l and 2l+1, so one row of the wave's
 // block is one scale group over the whole wave, as in the stand-alone
 // backward (relax_device.hpp). The four waves walk the same rows, so a
@@ -43,11 +44,11 @@ constexpr int kFT = 256;                 // threads per workgroup
 constexpr int kTileRows = 32;
 constexpr int kGroup = 128;              // columns per wave: one scale group
 constexpr int kTileCols = 4 * kGroup;
-constexpr int kSlabStride = kGroup + 8;  // floats per slab row
+constexpr int kSlabStride = kGroup + 4;  // floats per slab row
 constexpr int kFusedMaxExperts = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Experts of one launch: expert e (expert0 + e of the batch) owns rows
 // [e*rpe, (e+1)*rpe) of the layer, R^T block e at element rpe*tok[e]
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(kFT, 2) void recon_relax_kernel(FusedBatch fb, Rela
     // A wave past the layer's last column has nothing to do (no workgroup
     // barrier follows).
     if (col0 >= fb.cols) return;
-    const int frow = lane & 31, h = lane >> 5;
+    const int frow = lane & 15, fq = lane >> 4;
 
     // Backward + Lion (+ next forward), one row (scale group) at a time.
     const int nrows = min(kTileRows, fb.rpe - row0);
@@ -166,11 +167,13 @@ __global__ __launch_bounds__(kFT, 2) void recon_relax_kernel(FusedBatch fb, Rela
     for (int q = 0; q < kRing - 1; ++q)
         if (q < nrows) load_in(q, ring[q]);
 
-    f32x16 acc[4];
+    f32x4 acc[2][8];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[a][b][r] = 0.0f;
 
     // G tile = R^T[rows] X^T[cols]^T over the expert's tokens. An expert
     // without tokens has an empty contraction: G = 0.
@@ -178,49 +181,53 @@ __global__ __launch_bounds__(kFT, 2) void recon_relax_kernel(FusedBatch fb, Rela
         const uint16_t* A = fb.RT + static_cast<int64_t>(fb.rpe) * fb.tok[e];
         const uint16_t* B = fb.XT + static_cast<int64_t>(fb.cols) * fb.tok[e];
         // A row past the expert reads a valid row; its results are dropped.
-        const int arow = min(row0 + frow, fb.rpe - 1);
-        const bf16x8* pa = reinterpret_cast<const bf16x8*>(A + static_cast<int64_t>(arow) * ne + 8 * h);
-        const bf16x8* pb[4];
+        const bf16x8* pa[2];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int a = 0; a < 2; ++a) {
+            const int arow = min(row0 + 16 * a + frow, fb.rpe - 1);
+            pa[a] = reinterpret_cast<const bf16x8*>(A + static_cast<int64_t>(arow) * ne + 8 * fq);
+        }
+        const bf16x8* pb[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
             pb[b] = reinterpret_cast<const bf16x8*>(
-                B + static_cast<int64_t>(col0 + 32 * b + frow) * ne + 8 * h);
-        // Slice s starts 16 s elements (two 8-element vectors) further on.
-        bf16x8 fa[4], fbv[4][4];
+                B + static_cast<int64_t>(col0 + 16 * b + frow) * ne + 8 * fq);
+        // Slice s starts 32 s elements (four 8-element vectors) further on.
+        bf16x8 fa[2][2], fbv[2][8];
         auto ld = [&](int s, int slot) {
-            fa[slot] = pa[2 * s];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) fbv[slot][b] = pb[b][2 * s];
+            for (int a = 0; a < 2; ++a) fa[slot][a] = pa[a][4 * s];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) fbv[slot][b] = pb[b][4 * s];
         };
         auto mm = [&](int slot) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot], fbv[slot][b], acc[b], 0, 0, 0);
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][a], fbv[slot][b],
+                                                                        acc[a][b], 0, 0, 0);
         };
-        const int S = ne / 16;   // a multiple of 4 (ne is a multiple of 64)
+        const int S = ne / 32;   // even (ne is a multiple of 64)
         ld(0, 0);
-        ld(1, 1);
-        for (int s = 0; s < S; s += 4) {
-            ld(s + 2, 2);
+        for (int s = 0; s < S; s += 2) {
+            ld(s + 1, 1);
             mm(0);
-            ld(s + 3, 3);
+            if (s + 2 < S) ld(s + 2, 0);
             mm(1);
-            if (s + 4 < S) {
-                ld(s + 4, 0);
-                ld(s + 5, 1);
-            }
-            mm(2);
-            mm(3);
         }
     }
 
-    // Accumulators -> slab: register r of block b is G[8(r/4) + 4h + r%4][32b + frow].
+    // Accumulators -> slab: register r of block (a, b) is
+    // G[16a + 4q + r][16b + frow].
     float* my = slab + wave * 32 * kSlabStride;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            my[(8 * (r >> 2) + 4 * h + (r & 3)) * kSlabStride + 32 * b + frow] = acc[b][r];
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                my[(16 * a + 4 * fq + r) * kSlabStride + 16 * b + frow] = acc[a][b][r];
     // The slab is the wave's own: its LDS operations complete in order, so
     // the reads below see these stores; the empty asm keeps the compiler from
     // moving memory accesses across.

@@ -13,12 +13,14 @@
 // taken in its epilogue, and the plain bf16 products of the block forward.
 //
 // Tiling: 256x256 output tile per workgroup of 4 waves (2x2), each wave a
-// 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 blocks (256 fp32
-// accumulators per lane). K advances 64 at a time through two LDS buffers
+// 128x128 sub-tile of 8x8 v_mfma_f32_16x16x32_bf16 blocks (256 fp32
+// accumulators per lane). The 16x16 blocks, rather than 4x4 blocks of
+// 32x32x16, move the same LDS bytes per flop and hold a higher shader clock
+// under sustained matrix load. K advances 64 at a time through two LDS buffers
 // (2 x 64 KiB): global loads for step k+1 are in flight while step k's
 // fragments are read from LDS. LDS rows are 128 bytes; the 16-byte chunk
 // index is XOR-swizzled with the row so both the stores (8 threads per row)
-// and the fragment reads (32 rows x 16 bytes per half-wave) are free of bank
+// and the fragment reads (16 rows x 16 bytes per quarter-wave) are free of bank
 // conflicts. Workgroups are renumbered so that consecutive tiles share an XCD
 // (the dispatcher deals workgroups round-robin over the 8 XCDs) and tiles are
 // ordered in groups of 4 tile-rows, which keeps each XCD's A and B panels in
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     static_assert(TBN == 256 || TBN == 128, "tile width 256 or 128");
     static_assert(!GROUPED || TBN == BN, "expert batches use the full tile");
     constexpr int WN = TBN / 2;      // wave tile width
-    constexpr int NB = WN / 32;      // 32-column MFMA blocks per wave
+    constexpr int NB = WN / 16;      // 16-column MFMA blocks per wave
     constexpr int QB = TBN / 32;     // DMA row groups of the B tile
     __shared__ uint4 sA0[BM * kChunks];
     __shared__ uint4 sB0[BN * kChunks];   // a 128-wide tile uses the first half
@@ -232,31 +234,42 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
             ob[q] = rowb < g.J ? static_cast<uint32_t>((static_cast<int64_t>(rowb) * g.ldb + lch * 8) * 2) : kOob;
     }
 
-    f32x16 acc[4][NB];
+    // Block (a, b) of the wave's accumulators is the 16x16 output block at
+    // rows 16a, columns 16b of its sub-tile.
+    f32x4 acc[8][NB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+            for (int r = 0; r < 4; ++r) acc[a][b][r] = 0.0f;
 
-    // Fragment addressing: lane reads row (lane & 31) of a 32-row block, chunk
-    // 2*kk + (lane >> 5) of the 64-wide K slice; block rows start at multiples
-    // of 32, so the swizzle term is swz(lane & 31).
-    const int frow = lane & 31;
-    const int fhalf = lane >> 5;
+    // Fragment addressing: lane reads row (lane & 15) of a 16-row block at
+    // chunk 4s + (lane >> 4) of the 64-wide K-step, i.e. k = 32s + 8 (lane >> 4)
+    // .. + 7 of slice s; block rows start at multiples of 16, so the swizzle
+    // term is swz(lane & 15).
+    const int frow = lane & 15;
+    const int fq = lane >> 4;
     const int fsw = swz(frow);
     const int rowA = wi * 128 + frow;
     const int rowB = wj * WN + frow;
 
-    // Fragment registers: one slot per 16-wide slice of the K-step (slice kk
-    // always lives in slot kk), fetched two slices ahead of its MFMAs.
-    bf16x8 fa[4][4], fb[4][NB];
-    auto read_a = [&](const uint4* t, int kk, int b) {
-        return __builtin_bit_cast(bf16x8, t[(rowA + 32 * b) * kChunks + ((2 * kk + fhalf) ^ fsw)]);
+    // Fragment registers: slot s holds slice s of a K-step (8 A blocks, NB B
+    // blocks); slice 1 is fetched during slice 0's MFMAs and the next step's
+    // slice 0 during slice 1's.
+    bf16x8 fa[2][8], fb[2][NB];
+    auto read_a = [&](const uint4* t, int s, int a) {
+        return __builtin_bit_cast(bf16x8, t[(rowA + 16 * a) * kChunks + ((4 * s + fq) ^ fsw)]);
     };
-    auto read_b = [&](const uint4* t, int kk, int b) {
-        return __builtin_bit_cast(bf16x8, t[(rowB + 32 * b) * kChunks + ((2 * kk + fhalf) ^ fsw)]);
+    auto read_b = [&](const uint4* t, int s, int b) {
+        return __builtin_bit_cast(bf16x8, t[(rowB + 16 * b) * kChunks + ((4 * s + fq) ^ fsw)]);
+    };
+    // Fragment read q of a slice: the B blocks first, then the A blocks, in
+    // the order the MFMAs consume them.
+    constexpr int kReads = 8 + NB;
+    auto fetch1 = [&](const uint4* tA, const uint4* tB, int s, int q) {
+        if (q < NB) fb[s][q] = read_b(tB, s, q);
+        else fa[s][q - NB] = read_a(tA, s, q - NB);
     };
     // DMA load d (0..15) of a K-step: A loads q = 0..7, then B's QB loads
     // (a 128-wide tile has 4: its last four slots load nothing).
@@ -270,67 +283,62 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_rs, (lds_void*)(nB + r0 * kChunks), 16,
                                                      ob[q], koff, 0, 0);
     };
-    // Two of the eight fragment reads of slice kk into its slot, in the
-    // order its MFMAs consume them: B blocks 0-1, B 2-3, A 0-1, A 2-3.
-    // With two B blocks (128-wide tile): B 0-1, A 0-1, A 2-3, nothing.
-    auto fetch2 = [&](const uint4* tA, const uint4* tB, int kk, int part) {
-        if constexpr (NB == 4) {
-            if (part < 2) {
-                fb[kk][2 * part] = read_b(tB, kk, 2 * part);
-                fb[kk][2 * part + 1] = read_b(tB, kk, 2 * part + 1);
-            } else {
-                fa[kk][2 * part - 4] = read_a(tA, kk, 2 * part - 4);
-                fa[kk][2 * part - 3] = read_a(tA, kk, 2 * part - 3);
-            }
-        } else {
-            if (part == 0) {
-                fb[kk][0] = read_b(tB, kk, 0);
-                fb[kk][1] = read_b(tB, kk, 1);
-            } else if (part < 3) {
-                fa[kk][2 * part - 2] = read_a(tA, kk, 2 * part - 2);
-                fa[kk][2 * part - 1] = read_a(tA, kk, 2 * part - 1);
-            }
-        }
-    };
+    // Work item i of n spread over `parts` sub-groups: sub-group p takes
+    // items [first(p), first(p + 1)).
+    auto first = [](int p, int n, int parts) { return (p * n + parts - 1) / parts; };
+    // Sub-group of slice 1 at which the workgroup hands this step's buffer
+    // over to the DMA: the fragment reads of slice 1 have had two sub-groups
+    // of MFMAs to land.
+    constexpr int kBar = 2;
 
-    // One K-step, issued as 16 sub-groups (slice kk, A block a) of two
-    // fragment reads and the 4 MFMAs of block a, pinned in this order by
-    // scheduling barriers so memory instructions drain between MFMAs.
-    // Slices 0-1 fetch slices 2-3 of this step. At the start of slice 2 all
-    // reads of this step's buffer are issued: after they land, the next
-    // step's buffer has landed, and the workgroup has synced, slices 2-3
-    // fetch slices 0-1 of the next step and load step k+2 into this step's
-    // buffer (two DMA loads per sub-group), about a full K-step ahead.
-    auto kstep = [&](auto has_next, auto has_next2, const uint4* tA, const uint4* tB,
-                     const uint4* nA, const uint4* nB, uint32_t knext2) {
-        constexpr bool kNext = decltype(has_next)::value;    // step k+1 exists
-        constexpr bool kNext2 = decltype(has_next2)::value;  // step k+2 exists
+    // One K-step: two 32-wide slices, each issued as 8 sub-groups (A block a:
+    // NB MFMAs) with their share of fragment reads and DMA loads, pinned in
+    // this order by scheduling barriers so memory instructions drain between
+    // MFMAs. Slice 0 fetches slice 1 of this step. At sub-group kBar of
+    // slice 1, once every read of this step's buffer has landed, the next
+    // step's buffer has landed and the workgroup has synced, the remaining
+    // sub-groups fetch the next step's slice 0 and load step k+2 into this
+    // step's buffer, about a full K-step ahead.
+    // Every step is the same code, which keeps the accumulators in their
+    // registers: the last step also syncs and fetches from the other buffer,
+    // and the last two load the contraction's final K-step again (in range)
+    // in place of steps k+2 past its end; neither result is read.
+    auto kstep = [&](const uint4* tA, const uint4* tB, const uint4* nA,
+                     const uint4* nB, uint32_t knext2) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int a = 0; a < 8; ++a) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                if (kk < 2) {
-                    fetch2(tA, tB, kk + 2, a);
-                } else if constexpr (kNext) {
-                    if (kk == 2 && a == 0) {
-                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                        wait_dma();
-                        bar();
-                    }
-                    fetch2(nA, nB, kk - 2, a);
-                    if constexpr (kNext2) {
-                        uint4* fA = const_cast<uint4*>(tA);
-                        uint4* fB = const_cast<uint4*>(tB);
-                        dma1(2 * (4 * (kk - 2) + a), knext2, fA, fB);
-                        dma1(2 * (4 * (kk - 2) + a) + 1, knext2, fA, fB);
-                    }
-                }
+            for (int q = 0; q < kReads; ++q)
+                if (q >= first(a, kReads, 8) && q < first(a + 1, kReads, 8)) fetch1(tA, tB, 1, q);
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][a], fb[kk][b],
-                                                                        acc[a][b], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int b = 0; b < NB; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[0][a], fb[0][b], acc[a][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+            if (a == kBar) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                wait_dma();
+                bar();
             }
+            if (a >= kBar) {
+                const int p = a - kBar;
+#pragma unroll
+                for (int q = 0; q < kReads; ++q)
+                    if (q >= first(p, kReads, 8 - kBar) && q < first(p + 1, kReads, 8 - kBar))
+                        fetch1(nA, nB, 0, q);
+                uint4* fA = const_cast<uint4*>(tA);
+                uint4* fB = const_cast<uint4*>(tB);
+#pragma unroll
+                for (int d = 0; d < 16; ++d)
+                    if (d >= first(p, 16, 8 - kBar) && d < first(p + 1, 16, 8 - kBar))
+                        dma1(d, knext2, fA, fB);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[1][a], fb[1][b], acc[a][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -338,7 +346,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     constexpr uint32_t kStep = BK * 2;   // bytes of one K-step along a row
     // An expert without tokens has an empty contraction: its output is zero.
     if (nk > 0) {
-        // Prologue: step 0 (waited for) and step 1 in flight; slices 0-1 fetched.
+        // Prologue: step 0 (waited for) and step 1 in flight; slice 0 fetched.
         dma_tile<8>(ra_rs, oa, 0, sA0, wave);
         dma_tile<QB>(rb_rs, ob, 0, sB0, wave);
         if (nk > 1) {
@@ -352,34 +360,21 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
         }
         bar();
 #pragma unroll
-        for (int part = 0; part < 4; ++part) {
-            fetch2(sA0, sB0, 0, part);
-            fetch2(sA0, sB0, 1, part);
-        }
-        int kt = 0;
-        for (; kt + 2 < nk; ++kt) {
+        for (int q = 0; q < kReads; ++q) fetch1(sA0, sB0, 0, q);
+        for (int kt = 0; kt < nk; ++kt) {
             const bool odd = kt & 1;
-            kstep(std::true_type{}, std::true_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0,
-                  odd ? sA0 : sA1, odd ? sB0 : sB1, static_cast<uint32_t>(kt + 2) * kStep);
-        }
-        if (kt + 1 < nk) {
-            const bool odd = kt & 1;
-            kstep(std::true_type{}, std::false_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0,
-                  odd ? sA0 : sA1, odd ? sB0 : sB1, 0u);
-            ++kt;
-        }
-        {
-            const bool odd = kt & 1;
-            kstep(std::false_type{}, std::false_type{}, odd ? sA1 : sA0, odd ? sB1 : sB0, nullptr,
-                  nullptr, 0u);
+            kstep(odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1,
+                  static_cast<uint32_t>(min(kt + 2, nk - 1)) * kStep);
         }
     }
-    // All waves are done with the operand buffers before the epilogue reuses them.
+    // The last steps' DMA loads have landed and all waves are done with the
+    // operand buffers before the epilogue reuses them.
+    wait_dma();
     __syncthreads();
 
     // Epilogue, one 32-row slab of the wave's 128x128 sub-tile at a time:
     // accumulators go to a private 32x128 fp32 LDS slab (register r of block
-    // (a, b) is C[8*(r/4) + 4*(lane/32) + r%4][32*b + lane%32]), then each
+    // (a, b) is C[16a + 4*(lane/16) + r][16b + lane%16]), then each
     // lane reads back 8 (bf16 output) or 4 (fp32 output) consecutive values of
     // one row and stores them as one 16-byte vector. N and K are multiples of
     // 8, so a vector is entirely inside or outside the matrix.
@@ -407,19 +402,20 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
         }
     };
     if constexpr (EPI == EPI_F32_GRAM) load_dv(0, dv[0]);
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    // Slab a of the wave (a compile-time index, so the accumulators stay in
+    // place).
+    auto slab_out = [&](auto slab_index) {
+        constexpr int a = decltype(slab_index)::value;
         if constexpr (EPI == EPI_F32_GRAM) {
             if (a + 1 < 4) load_dv(a + 1, dv[(a + 1) & 1]);
         }
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 8 * (r >> 2) + 4 * fhalf + (r & 3);
-                slab[row * kSlab + 32 * b + frow] = acc[a][b][r];
-            }
-        }
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    slab[(16 * h + 4 * fq + r) * kSlab + 16 * b + frow] = acc[2 * a + h][b][r];
         __syncthreads();
         if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_BF16 || EPI == EPI_BF16_LOSS_OFF) {
             // 16 lanes per 128-value row: 8 values -> one 16-byte bf16 store.
@@ -481,7 +477,11 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
             }
         }
         __syncthreads();
-    }
+    };
+    slab_out(std::integral_constant<int, 0>{});
+    slab_out(std::integral_constant<int, 1>{});
+    slab_out(std::integral_constant<int, 2>{});
+    slab_out(std::integral_constant<int, 3>{});
     if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_F32_GRAM || EPI == EPI_BF16_LOSS_OFF) {
         // Fixed-order reduction: wave butterfly, then waves 0..3 in order.
         __shared__ float red[NT / 64];
