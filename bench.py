@@ -544,6 +544,42 @@ def run_workload(name: str, args, dev, steps: int, warmup: int, headline: bool):
     return res, data
 
 
+def gemm_vs_vendor(I: int, J: int, K: int, dev, steps: int, warmup: int):
+    """The plain bf16 NT product on seeded N(0,1) operands: this library's
+    kernel and torch's matmul (hipBLASLt on ROCm) alternately, ``steps``
+    timed calls each after ``warmup``, HIP events on the current stream.
+    Prints one JSON line; the two outputs are compared (max relative
+    difference) so the comparison is between products of the same result."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    A = torch.randn(I, K, device=dev, generator=gen).to(torch.bfloat16)
+    B = torch.randn(J, K, device=dev, generator=gen).to(torch.bfloat16)
+    C = torch.empty(I, J, device=dev, dtype=torch.bfloat16)
+    C2 = torch.empty(I, J, device=dev, dtype=torch.bfloat16)
+    Bt = B.t()
+    ours = lambda: g.gsq_matmul_nt_bf16(I, J, K, A, K, B, K, C, J)
+    vendor = lambda: torch.matmul(A, Bt, out=C2)
+    res = {}
+    for rep in range(2):
+        for name, f in (("ours", ours), ("hipblaslt", vendor)):
+            for _ in range(warmup):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            if rep == 1:
+                res[name] = {"us": us, "TFLOP/s": 2.0 * I * J * K / us / 1e6}
+    d = (C.float() - C2.float()).abs().max().item() / max(C2.float().abs().max().item(), 1e-30)
+    print(json.dumps({"shape": [I, J, K], "steps": steps, **res, "max_rel_diff": d}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -581,6 +617,10 @@ def main():
                          "(gsq_recon_bwd_lion_fwd) instead of the separate calls")
     ap.add_argument("--no-ab", action="store_true",
                     help="skip timing the other form of the headline step (fused / separate)")
+    ap.add_argument("--gemm-vs-vendor", nargs=3, type=int, metavar=("I", "J", "K"),
+                    help="time the plain bf16 NT product C = A B^T (I x K times J x K) with this "
+                         "library's kernel and with torch's matmul (hipBLASLt) in one process, "
+                         "for side-by-side profiles, and exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 counter runs of this script into "
                          "profiles/traffic_<workload>.json and exit")
@@ -603,6 +643,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.block:
         block_bench(args, dev)
+        return
+    if args.gemm_vs_vendor:
+        gemm_vs_vendor(*args.gemm_vs_vendor, dev, args.steps, args.warmup)
         return
     head, data = run_workload(args.workload, args, dev, args.steps, args.warmup, headline=True)
     wl = data["workload"]
