@@ -16,9 +16,12 @@
 // 128x128 sub-tile of 8x8 v_mfma_f32_16x16x32_bf16 blocks (256 fp32
 // accumulators per lane). The 16x16 blocks, rather than 4x4 blocks of
 // 32x32x16, move the same LDS bytes per flop and hold a higher shader clock
-// under sustained matrix load. K advances 64 at a time through two LDS buffers
-// (2 x 64 KiB): global loads for step k+1 are in flight while step k's
-// fragments are read from LDS. LDS rows are 128 bytes; the 16-byte chunk
+// under sustained matrix load. K advances 64 at a time; the A tiles (32 KiB
+// a step) alternate between two LDS buffers and the B tiles rotate through
+// three, 160 KiB in all: global loads run a step ahead of the fragment reads,
+// and half of a step's B loads can be issued a slice before the A buffer they
+// wait behind is free, which spreads the loads over more of the step. LDS
+// rows are 128 bytes; the 16-byte chunk
 // index is XOR-swizzled with the row so both the stores (8 threads per row)
 // and the fragment reads (16 rows x 16 bytes per quarter-wave) are free of bank
 // conflicts. Workgroups are renumbered so that consecutive tiles share an XCD
@@ -187,13 +190,19 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     constexpr int WN = TBN / 2;      // wave tile width
     constexpr int NB = WN / 16;      // 16-column MFMA blocks per wave
     constexpr int QB = TBN / 32;     // DMA row groups of the B tile
+    // A tiles in two buffers, B tiles in a ring of three (a 128-wide tile
+    // uses the first half of each): 160 KiB, the whole LDS.
     __shared__ uint4 sA0[BM * kChunks];
-    __shared__ uint4 sB0[BN * kChunks];   // a 128-wide tile uses the first half
     __shared__ uint4 sA1[BM * kChunks];
-    __shared__ uint4 sB1[BN * kChunks];
+    __shared__ uint4 sBr[3 * BN * kChunks];
+    uint4* const sB0 = sBr;
+    uint4* const sB1 = sBr + BN * kChunks;
+    uint4* const sB2 = sBr + 2 * BN * kChunks;
 
     if (g.fin_loss != nullptr && blockIdx.x == 0) {
-        __shared__ double fred[NT];
+        // In the third B buffer, which no load writes before the prologue's
+        // barrier.
+        double* fred = reinterpret_cast<double*>(sB2);
         double fs = 0.0;
         for (int i = threadIdx.x; i < g.fin_n; i += NT) fs += static_cast<double>(g.fin_partials[i]);
         fred[threadIdx.x] = fs;
@@ -290,26 +299,36 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     // over to the DMA: the fragment reads of slice 1 have had two sub-groups
     // of MFMAs to land.
     constexpr int kBar = 2;
+    // B-tile loads of step k+2 issued in step k's first slice, half of them:
+    // the B tiles rotate through three buffers, so these have their buffer
+    // free a slice before the barrier frees the A buffer for the rest.
+    constexpr int kB0 = QB / 2;
 
     // One K-step: two 32-wide slices, each issued as 8 sub-groups (A block a:
     // NB MFMAs) with their share of fragment reads and DMA loads, pinned in
     // this order by scheduling barriers so memory instructions drain between
-    // MFMAs. Slice 0 fetches slice 1 of this step. At sub-group kBar of
-    // slice 1, once every read of this step's buffer has landed, the next
-    // step's buffer has landed and the workgroup has synced, the remaining
-    // sub-groups fetch the next step's slice 0 and load step k+2 into this
-    // step's buffer, about a full K-step ahead.
+    // MFMAs. Slice 0 fetches slice 1 of this step and issues kB0 of step
+    // k+2's B-tile loads into the B ring. At sub-group kBar of slice 1, once
+    // every read of this step's buffers has landed, the next step has landed
+    // and the workgroup has synced, the remaining sub-groups fetch the next
+    // step's slice 0 and issue step k+2's other loads (its A tile into this
+    // step's A buffer), about a full K-step ahead.
     // Every step is the same code, which keeps the accumulators in their
     // registers: the last step also syncs and fetches from the other buffer,
     // and the last two load the contraction's final K-step again (in range)
     // in place of steps k+2 past its end; neither result is read.
     auto kstep = [&](const uint4* tA, const uint4* tB, const uint4* nA,
-                     const uint4* nB, uint32_t knext2) {
+                     const uint4* nB, uint4* bB2, uint32_t knext2) {
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
 #pragma unroll
             for (int q = 0; q < kReads; ++q)
                 if (q >= first(a, kReads, 8) && q < first(a + 1, kReads, 8)) fetch1(tA, tB, 1, q);
+            // The last kB0 B-tile loads of step k+2, one per sub-group, into
+            // the ring buffer that step k-1 used (free since its barrier).
+#pragma unroll
+            for (int d = 8 + QB - kB0; d < 8 + QB; ++d)
+                if (a == d - (8 + QB - kB0)) dma1(d, knext2, nullptr, bB2);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[0][a], fb[0][b], acc[a][b], 0, 0, 0);
@@ -318,8 +337,10 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
             if (a == kBar) {
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                wait_dma();
+                // Step k+1 has landed; the kB0 loads of step k+2 issued in
+                // slice 0 may still be in flight.
+                if constexpr (kB0 == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)" ::: "memory");
                 bar();
             }
             if (a >= kBar) {
@@ -328,12 +349,14 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
                 for (int q = 0; q < kReads; ++q)
                     if (q >= first(p, kReads, 8 - kBar) && q < first(p + 1, kReads, 8 - kBar))
                         fetch1(nA, nB, 0, q);
+                // The other loads of step k+2: the A tile into this step's
+                // buffer, the rest of the B tile into the ring.
                 uint4* fA = const_cast<uint4*>(tA);
-                uint4* fB = const_cast<uint4*>(tB);
+                constexpr int kD1 = 8 + QB - kB0;
 #pragma unroll
-                for (int d = 0; d < 16; ++d)
-                    if (d >= first(p, 16, 8 - kBar) && d < first(p + 1, 16, 8 - kBar))
-                        dma1(d, knext2, fA, fB);
+                for (int d = 0; d < kD1; ++d)
+                    if (d >= first(p, kD1, 8 - kBar) && d < first(p + 1, kD1, 8 - kBar))
+                        dma1(d, knext2, fA, bB2);
             }
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -361,10 +384,15 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
         bar();
 #pragma unroll
         for (int q = 0; q < kReads; ++q) fetch1(sA0, sB0, 0, q);
+        uint4* b0 = sB0;   // B ring: steps kt, kt+1, kt+2
+        uint4* b1 = sB1;
+        uint4* b2 = sB2;
         for (int kt = 0; kt < nk; ++kt) {
             const bool odd = kt & 1;
-            kstep(odd ? sA1 : sA0, odd ? sB1 : sB0, odd ? sA0 : sA1, odd ? sB0 : sB1,
+            kstep(odd ? sA1 : sA0, b0, odd ? sA0 : sA1, b1, b2,
                   static_cast<uint32_t>(min(kt + 2, nk - 1)) * kStep);
+            uint4* const t = b0;
+            b0 = b1; b1 = b2; b2 = t;
         }
     }
     // The last steps' DMA loads have landed and all waves are done with the
@@ -382,6 +410,7 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
                                         // start 16 bytes apart in the banks
     // One 32 KiB buffer per wave.
     float* slab = reinterpret_cast<float*>(wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1);
+    float* red = reinterpret_cast<float*>(sB2);   // the loss partial's wave sums
     const int grow0 = i0 + wi * 128;
     const int gcol0 = j0 + wj * WN;
     float lsum = 0.0f;
@@ -484,7 +513,6 @@ __global__ __launch_bounds__(NT) void gemm_nt_kernel(GemmArgs g, ExpertBatch eb)
     slab_out(std::integral_constant<int, 3>{});
     if constexpr (EPI == EPI_BF16_LOSS || EPI == EPI_F32_GRAM || EPI == EPI_BF16_LOSS_OFF) {
         // Fixed-order reduction: wave butterfly, then waves 0..3 in order.
-        __shared__ float red[NT / 64];
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) lsum += __shfl_xor(lsum, m, 64);
         if (lane == 0) red[wave] = lsum;
