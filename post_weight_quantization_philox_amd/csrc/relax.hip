@@ -15,6 +15,10 @@ using namespace relax;
 
 constexpr int kThreads = 256;
 
+// Coordinates per thread in the backward + Lion kernel: one on the 2-bit
+// grid (a scale group then spans two waves), the relax default otherwise.
+template <int GRID> struct BwdN { static constexpr int N = GRID == GSQ_GRID_INT2 ? 1 : GridT<GRID>::N; };
+
 // ---------------------------------------------------------------------------
 // Forward: dW = s*w_hat - W, bf16.
 // ---------------------------------------------------------------------------
@@ -56,12 +60,19 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
     float* __restrict__ gl_dbg, float* __restrict__ gs_dbg, const void* __restrict__ W,
     uint32_t next_step, TauK tk_next, uint16_t* __restrict__ dW) {
     constexpr int L = GridT<GRID>::L;
-    constexpr int N = GridT<GRID>::N;
+    constexpr int N = BwdN<GRID>::N;
     constexpr int P = 128 / N;   // lanes per scale group
-    const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x) * N;
-    // Whole scale groups (P threads) are either in range or not, so the
-    // shuffles below never read a lane that returned here.
-    if (i0 >= mk) return;
+    uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x) * N;
+    // Whole scale groups (P threads) are either in range or not. A group
+    // spanning two waves meets its partner at a workgroup barrier, so an
+    // out-of-range group works on the group before it and stores nothing.
+    bool live = true;
+    if constexpr (P > 64) {
+        live = i0 < mk;
+        if (!live) i0 -= 128;
+    } else if (i0 >= mk) {
+        return;
+    }
     const Idx<O32> ix{i0};
     float g[N];
     loadv<N>(ix.at(G), g);
@@ -75,19 +86,43 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
     const float s = scales[grp];
     uint32_t cw = 0;
     if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = load_codes<N>(codes, ix);
-    float gsum = bwd_lion_coords<GRID, DBG, O32>(g, l, m, s, cw, i0, step, sid, key, tk, lkl,
-                                                 gl_dbg, ix, mk);
+    float what = 0.0f;
+    float gsum = bwd_lion_coords<GRID, DBG, O32, N>(g, l, m, s, cw, i0, step, sid, key, tk, lkl,
+                                                    gl_dbg, ix, mk, &what);
+    if (live) {
 #pragma unroll
-    for (int k = 0; k < L; ++k) {
-        storev<N>(ix.at(logits, mk, k), l[k]);
-        storev<N>(ix.at(mom, mk, k), m[k]);
+        for (int k = 0; k < L; ++k) {
+            storev<N>(ix.at(logits, mk, k), l[k]);
+            storev<N>(ix.at(mom, mk, k), m[k]);
+        }
     }
     // Group sum, taken from the group's first lane so that every lane applies
     // the same Lion update to the shared scale.
-    gsum = __shfl(group_sum<P>(gsum), group_lane0<P>(), 64);
+    if constexpr (P <= 64) {
+        gsum = __shfl(group_sum<P>(gsum), group_lane0<P>(), 64);
+    } else {
+        // The same additions, in the same order, as with two coordinates per
+        // lane (the fused product's layout): lanes 2i and 2i+1 first form
+        // fma(g_{2i+1}, w_hat_{2i+1}, g_{2i} w_hat_{2i}), the pair's term;
+        // then the butterfly over the 64 pair terms, whose first stage (pairs
+        // 32 apart) joins the group's two waves through LDS and whose other
+        // stages are lane shuffles 32, 16, 8, 4 and 2 apart.
+        const int lane = threadIdx.x & 63;
+        const float t_even = __shfl(gsum, lane & ~1, 64);
+        const float g_odd = __shfl(g[0], lane | 1, 64);
+        const float w_odd = __shfl(what, lane | 1, 64);
+        float v = __builtin_fmaf(g_odd, w_odd, t_even);
+        __shared__ float xs[kThreads];
+        xs[threadIdx.x] = v;
+        __syncthreads();
+        v += xs[threadIdx.x ^ 64];
+#pragma unroll
+        for (int mm = 32; mm >= 2; mm >>= 1) v += __shfl_xor(v, mm, 64);
+        gsum = __shfl(v, 0, 64);
+    }
     float sn = s, smn = scale_mom[grp];
     lion_update(sn, smn, gsum, lks);
-    if ((threadIdx.x & (P - 1)) == 0) {
+    if (live && (threadIdx.x & (P - 1)) == 0) {
         scales[grp] = sn;
         scale_mom[grp] = smn;
         if constexpr (DBG) gs_dbg[grp] = gsum;
@@ -97,8 +132,8 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
         float w[N];
         load_w<N>(W, WBF16, ix, w);
         float out[N];
-        fwd_coords<GRID>(l, sn, cw, i0, next_step, sid, key, tk_next, out);
-        store_dw<N>(dW, ix, out, w);
+        fwd_coords<GRID, N>(l, sn, cw, i0, next_step, sid, key, tk_next, out);
+        if (live) store_dw<N>(dW, ix, out, w);
     }
 }
 
@@ -262,6 +297,15 @@ hipError_t launch_init_rtn(const LayerDesc& d, const void* W, float* scales, uin
 inline bool off32(const LayerDesc& d) { return d.mk * 4 <= 0xFFFFFFF0ull; }
 
 // Threads of the relax kernels: one per N coordinates.
+inline uint64_t bwd_threads(const LayerDesc& d) {
+    switch (d.grid) {
+        case GSQ_GRID_INT2: return d.mk / BwdN<GSQ_GRID_INT2>::N;
+        case GSQ_GRID_INT3: return d.mk / BwdN<GSQ_GRID_INT3>::N;
+        case GSQ_GRID_TERNARY: return d.mk / BwdN<GSQ_GRID_TERNARY>::N;
+        default: return d.mk / BwdN<GSQ_GRID_INT3_LOCAL>::N;
+    }
+}
+
 inline uint64_t relax_threads(const LayerDesc& d) {
     switch (d.grid) {
         case GSQ_GRID_INT2: return d.mk / GridT<GSQ_GRID_INT2>::N;
@@ -302,7 +346,7 @@ hipError_t launch_relax_bwd_lion(const LayerDesc& d, const float* G, float* logi
                                  uint32_t step, TauK tk, LionK lkl, LionK lks,
                                  float* gl_dbg, float* gs_dbg, const void* W, uint32_t next_step,
                                  TauK tk_next, uint16_t* dW, hipStream_t st) {
-    const unsigned nb = blocks_for(relax_threads(d));
+    const unsigned nb = blocks_for(bwd_threads(d));
     const bool dbg = gl_dbg != nullptr || gs_dbg != nullptr;
     const bool fwd = dW != nullptr;
     const bool o32 = off32(d);

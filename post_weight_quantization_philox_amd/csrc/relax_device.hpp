@@ -21,6 +21,14 @@
 namespace gsq {
 namespace relax {
 
+// No implicit contraction of a product into a following sum in this code: a
+// separately rounded product and sum (v_k - w_hat with w_hat = num / sum, or
+// s * w_hat - w) would otherwise be fused in some kernels and not in others,
+// depending on how each instantiation is scheduled. Written-out fmaf calls
+// are kept. Every kernel that runs these functions, in either layout, then
+// gets the same bits.
+#pragma clang fp contract(off)
+
 template <int GRID> struct GridT;
 // L logits per coordinate, q_max, code bits, and N coordinates per thread in
 // the relax kernels.
@@ -76,11 +84,13 @@ __device__ __forceinline__ void st_nt(T v, T* p) { __builtin_nontemporal_store(v
 // N = 2 or 4 consecutive values as one vector access.
 template <int N>
 __device__ __forceinline__ void loadv(const float* p, float (&v)[N]) {
-    if constexpr (N == 4) {
+    if constexpr (N == 1) {
+        v[0] = ld_nt(p);
+    } else if constexpr (N == 4) {
         const f32x4_t x = ld_nt(reinterpret_cast<const f32x4_t*>(p));
         v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
     } else {
-        static_assert(N == 2, "2 or 4 coordinates per thread");
+        static_assert(N == 2, "1, 2 or 4 coordinates per thread");
         const f32x2_t x = ld_nt(reinterpret_cast<const f32x2_t*>(p));
         v[0] = x.x; v[1] = x.y;
     }
@@ -88,7 +98,9 @@ __device__ __forceinline__ void loadv(const float* p, float (&v)[N]) {
 
 template <int N>
 __device__ __forceinline__ void storev(float* p, const float (&v)[N]) {
-    if constexpr (N == 4) {
+    if constexpr (N == 1) {
+        st_nt(v[0], p);
+    } else if constexpr (N == 4) {
         st_nt(f32x4_t{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4_t*>(p));
     } else {
         st_nt(f32x2_t{v[0], v[1]}, reinterpret_cast<f32x2_t*>(p));
@@ -99,7 +111,9 @@ template <int N, bool O32>
 __device__ __forceinline__ void load_w(const void* W, bool bf16, Idx<O32> ix, float (&w)[N]) {
     if (bf16) {
         const uint16_t* p = ix.at(static_cast<const uint16_t*>(W));
-        if constexpr (N == 4) {
+        if constexpr (N == 1) {
+            w[0] = bf16_lo(static_cast<uint32_t>(ld_nt(p)));
+        } else if constexpr (N == 4) {
             const u32x2_t v = ld_nt(reinterpret_cast<const u32x2_t*>(p));
             w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x); w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
         } else {
@@ -114,7 +128,8 @@ __device__ __forceinline__ void load_w(const void* W, bool bf16, Idx<O32> ix, fl
 // The N warm-start codes (one byte each) as one little-endian word.
 template <int N, bool O32>
 __device__ __forceinline__ uint32_t load_codes(const uint8_t* codes, Idx<O32> ix) {
-    if constexpr (N == 4) return ld_nt(reinterpret_cast<const uint32_t*>(ix.at(codes)));
+    if constexpr (N == 1) return ld_nt(ix.at(codes));
+    else if constexpr (N == 4) return ld_nt(reinterpret_cast<const uint32_t*>(ix.at(codes)));
     else return ld_nt(reinterpret_cast<const uint16_t*>(ix.at(codes)));
 }
 
@@ -122,7 +137,9 @@ __device__ __forceinline__ uint32_t load_codes(const uint8_t* codes, Idx<O32> ix
 template <int N, bool O32>
 __device__ __forceinline__ void store_dw(uint16_t* dW, Idx<O32> ix, const float (&out)[N],
                                          const float (&w)[N]) {
-    if constexpr (N == 4) {
+    if constexpr (N == 1) {
+        st_nt(static_cast<uint16_t>(pack_bf16x2(out[0] - w[0], 0.0f) & 0xFFFFu), ix.at(dW));
+    } else if constexpr (N == 4) {
         const u32x2_t o = {pack_bf16x2(out[0] - w[0], out[1] - w[1]),
                            pack_bf16x2(out[2] - w[2], out[3] - w[3])};
         st_nt(o, reinterpret_cast<u32x2_t*>(ix.at(dW)));
@@ -142,10 +159,11 @@ __device__ __forceinline__ void store4(float* p, const float v[4]) {
 
 template <int C> using Ci = std::integral_constant<int, C>;
 
-// Calls f(Ci<0>{}) .. f(Ci<N-1>{}) in order (N = 2 or 4).
+// Calls f(Ci<0>{}) .. f(Ci<N-1>{}) in order (N = 1, 2 or 4).
 template <int N, typename F>
 __device__ __forceinline__ void forN(F&& f) {
-    f(Ci<0>{}); f(Ci<1>{});
+    f(Ci<0>{});
+    if constexpr (N >= 2) f(Ci<1>{});
     if constexpr (N == 4) { f(Ci<2>{}); f(Ci<3>{}); }
 }
 
@@ -221,17 +239,17 @@ __device__ __forceinline__ void relax_coord(const float (&l)[GridT<GRID>::L], co
 // place): dL/dl from G (g), the old scale s and the step's regenerated noise,
 // then one Lion update per logit. Each coordinate's gradient goes straight
 // into its Lion update, so no gradient array stays live. Returns the
-// thread's part of the scale gradient, sum_c g_c * w_hat_c.
-template <int GRID, bool DBG, bool O32>
-__device__ __forceinline__ float bwd_lion_coords(const float (&g)[GridT<GRID>::N],
-                                                 float (&l)[GridT<GRID>::L][GridT<GRID>::N],
-                                                 float (&m)[GridT<GRID>::L][GridT<GRID>::N],
+// thread's part of the scale gradient, sum_c g_c * w_hat_c (fma in
+// coordinate order from 0); *what_last receives the last coordinate's w_hat.
+template <int GRID, bool DBG, bool O32, int N = GridT<GRID>::N>
+__device__ __forceinline__ float bwd_lion_coords(const float (&g)[N],
+                                                 float (&l)[GridT<GRID>::L][N],
+                                                 float (&m)[GridT<GRID>::L][N],
                                                  float s, uint32_t cw, uint64_t i0, uint32_t step,
                                                  uint32_t sid, Key key, TauK tk, LionK lkl,
                                                  float* __restrict__ gl_dbg, Idx<O32> ix,
-                                                 uint64_t mk) {
+                                                 uint64_t mk, float* what_last = nullptr) {
     constexpr int L = GridT<GRID>::L;
-    constexpr int N = GridT<GRID>::N;
     float gsum = 0.0f;
     NoiseFor<L, N> ns(i0, step, sid, key);
     const float gs_tau = s * tk.invtau;
@@ -256,6 +274,7 @@ __device__ __forceinline__ float bwd_lion_coords(const float (&g)[GridT<GRID>::N
             for (int k = 0; k < L; ++k) glc[k] = gn * r.e[k] * (r.v[k] - r.what);
         }
         gsum = __builtin_fmaf(g[c], r.what, gsum);
+        if (what_last != nullptr) *what_last = r.what;
 #pragma unroll
         for (int k = 0; k < L; ++k) {
             if constexpr (DBG) ix.at(gl_dbg, mk, k)[c] = glc[k];
@@ -267,13 +286,12 @@ __device__ __forceinline__ float bwd_lion_coords(const float (&g)[GridT<GRID>::N
 
 // Relaxed forward of the thread's N coordinates from logits l and scale s:
 // out_c = s * w_hat_c.
-template <int GRID>
-__device__ __forceinline__ void fwd_coords(const float (&l)[GridT<GRID>::L][GridT<GRID>::N],
+template <int GRID, int N = GridT<GRID>::N>
+__device__ __forceinline__ void fwd_coords(const float (&l)[GridT<GRID>::L][N],
                                            float s, uint32_t cw, uint64_t i0, uint32_t step,
                                            uint32_t sid, Key key, TauK tk,
-                                           float (&out)[GridT<GRID>::N]) {
+                                           float (&out)[N]) {
     constexpr int L = GridT<GRID>::L;
-    constexpr int N = GridT<GRID>::N;
     NoiseFor<L, N> ns(i0, step, sid, key);
     forN<N>([&](auto cc) {
         constexpr int c = decltype(cc)::value;
