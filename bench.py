@@ -506,13 +506,12 @@ def run_workload(name: str, args, dev, steps: int, warmup: int, headline: bool):
                      "note": "warm start, X^T and state allocation, once per layer, not in the step"}}
     if separate is not None:
         res["ab_other_path"] = separate
-    if name == "qproj4096_int2" and not unfused:
+    del solver
+    torch.cuda.empty_cache()
+    if wl.experts == 1 and not unfused and 2 * N > K:
         # The same step with the objective in Gram form (H = X^T X formed
         # once, untimed; one product of 2*M*K*K flops per step instead of two
-        # of 2*N*M*K), on a fresh solver; then the two-product solve captured
-        # as one HIP graph.
-        del solver
-        torch.cuda.empty_cache()
+        # of 2*N*M*K, fewer flops when N > K/2), on a fresh solver.
         gsol = LayerSolver(Wd, Xd, wl.grid, seed=0, stream_id=0, recon="gram", lion=lion)
         g_el, g_rec, g_fus = time_fused(gsol, taus, warmup, steps, stream)
         gram_flops = 2.0 * M * K * K
@@ -524,6 +523,8 @@ def run_workload(name: str, args, dev, steps: int, warmup: int, headline: bool):
             "last_loss": float(gsol.loss.item())}
         del gsol
         torch.cuda.empty_cache()
+    if name == "qproj4096_int2" and not unfused:
+        # The two-product solve captured as one HIP graph.
         csol = LayerSolver(Wd, Xd, wl.grid, seed=0, stream_id=0, lion=lion)
         graph = csol.capture_solve(steps)
         graph.replay()
@@ -537,8 +538,6 @@ def run_workload(name: str, args, dev, steps: int, warmup: int, headline: bool):
                         "ms_per_step": c_el * 1e3 / steps,
                         "note": "the two-product step, whole solve replayed as one HIP graph"}
         del csol, graph
-    else:
-        del solver
     del Wd, Xd
     torch.cuda.empty_cache()
     return res, data
