@@ -6,12 +6,13 @@
 // Thread mapping: one thread owns N consecutive coordinates i0..i0+N-1 of the
 // flattened layer (i0 a multiple of N), so every planar logit / momentum
 // plane is read and written as one N*4-byte vector per thread. 128/N threads
-// cover one scale group of 128 coordinates and reduce it with lane shuffles.
-// N is 2 for every grid: 8-byte vectors per plane stream faster than 16-byte
-// ones on this access mix, and a thread holds half the registers, so more
-// waves are in flight. With 5 logits (local shift) two coordinates are 10
-// noise words, which start at word 0 or 2 of a Philox block (NoiseStreamU);
-// the other grids' words are whole blocks (NoiseStream).
+// cover one scale group of 128 coordinates. GridT<>::N is 2 for every grid
+// (8-byte vectors per plane stream faster than 16-byte ones on this access
+// mix, and a thread holds half the registers of N = 4); the backward + Lion
+// kernel instantiates the 2-bit and full 3-bit grids with N = 1 instead
+// (relax.hip). With 5 logits (local shift) two coordinates are 10 noise
+// words, which start at word 0 or 2 of a Philox block (NoiseStreamU); the
+// other grids' words are whole blocks (NoiseStream).
 #pragma once
 
 #include <type_traits>
@@ -81,7 +82,7 @@ __device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_lo
 template <typename T>
 __device__ __forceinline__ void st_nt(T v, T* p) { __builtin_nontemporal_store(v, p); }
 
-// N = 2 or 4 consecutive values as one vector access.
+// N = 1, 2 or 4 consecutive values as one access.
 template <int N>
 __device__ __forceinline__ void loadv(const float* p, float (&v)[N]) {
     if constexpr (N == 1) {
