@@ -128,8 +128,12 @@ __global__ __launch_bounds__(kFT, 2) void recon_relax_kernel(FusedBatch fb, Rela
     const int nwg = gridDim.x;
     const int wg = blockIdx.x;
     const int logical = (nwg & 7) == 0 ? (wg & 7) * (nwg >> 3) + (wg >> 3) : wg;
+    // The expert: how many later starts lie at or below `logical` (wg0 is
+    // nondecreasing), unrolled so the table is read with wide scalar loads.
     int e = 0;
-    for (int k = 1; k < fb.n; ++k) e = logical >= fb.wg0[k] ? k : e;
+#pragma unroll
+    for (int k = 1; k < kFusedMaxExperts; ++k) e += (k < fb.n && logical >= fb.wg0[k]) ? 1 : 0;
+    e = __builtin_amdgcn_readfirstlane(e);   // uniform: keeps the addressing scalar
     const int local = logical - fb.wg0[e];
     const int ti = local / fb.tiles_j, tj = local % fb.tiles_j;
     const int ne = fb.tok[e + 1] - fb.tok[e];
