@@ -94,8 +94,10 @@ __global__ __launch_bounds__(kThreads) void relax_bwd_lion_kernel(
     uint32_t cw = 0;
     if constexpr (GRID == GSQ_GRID_INT3_LOCAL) cw = load_codes<N>(codes, ix);
     float what = 0.0f;
+    // An out-of-range group recomputes its neighbour while that neighbour's
+    // threads may already be storing: it writes no debug gradients either.
     float gsum = bwd_lion_coords<GRID, DBG, O32, N>(g, l, m, s, cw, i0, step, sid, key, tk, lkl,
-                                                    gl_dbg, ix, mk, &what);
+                                                    live ? gl_dbg : nullptr, ix, mk, &what);
     if (live) {
 #pragma unroll
         for (int k = 0; k < L; ++k) {

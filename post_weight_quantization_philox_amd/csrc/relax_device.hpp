@@ -278,7 +278,9 @@ __device__ __forceinline__ float bwd_lion_coords(const float (&g)[N],
         if (what_last != nullptr) *what_last = r.what;
 #pragma unroll
         for (int k = 0; k < L; ++k) {
-            if constexpr (DBG) ix.at(gl_dbg, mk, k)[c] = glc[k];
+            if constexpr (DBG) {
+                if (gl_dbg != nullptr) ix.at(gl_dbg, mk, k)[c] = glc[k];
+            }
             lion_update(l[k][c], m[k][c], glc[k], lkl);
         }
     });
