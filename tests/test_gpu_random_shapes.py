@@ -1,0 +1,54 @@
+"""Parity on seeded random shapes: grouped products over random expert counts
+(up to 70, so some batches take two launches) and random token blocks
+(empty ones included), and the relax backward + Lion on random row counts and
+group counts (odd numbers of scale groups included). Each case runs the same
+checks, with the same tolerances, as the fixed-shape tests in
+test_gpu_parity.py."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_gpu_parity as parity
+from tests.gpu_util import device
+
+pytestmark = pytest.mark.gpu
+
+
+def _recon_cases(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        # the first case takes more experts than one grouped launch holds
+        E = int(rng.integers(65, 71)) if not cases else int(rng.integers(1, 71))
+        rpe = int(rng.choice([32, 64, 160, 256, 288]))
+        K = int(rng.choice([128, 256, 384, 640]))
+        offs = [0] + np.cumsum(rng.choice([0, 64, 128, 192, 320], E)).tolist()
+        if offs[-1] == 0:
+            continue
+        cases.append((E * rpe, int(offs[-1]), K, offs if E > 1 else None))
+    return cases
+
+
+def _bwd_cases(n, seed=2025):
+    rng = np.random.default_rng(seed)
+    grids = [oracle.GRID_INT2, oracle.GRID_TERNARY, oracle.GRID_INT3_LOCAL, oracle.GRID_INT3]
+    return [(grids[i % 4], (int(rng.integers(1, 40)), 128 * int(rng.integers(1, 7))),
+             float(rng.choice([1.0, 0.3, 0.05]))) for i in range(n)]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+@pytest.mark.parametrize("M,N,K,offs", _recon_cases(8),
+                         ids=lambda v: None if not isinstance(v, list) else f"E{len(v) - 1}")
+def test_recon_random_shapes(dev, M, N, K, offs):
+    parity.test_recon_loss_grad(dev, M, N, K, offs)
+
+
+@pytest.mark.parametrize("grid,shape,tau", _bwd_cases(8),
+                         ids=lambda v: f"{v[0]}x{v[1]}" if isinstance(v, tuple) else str(v))
+def test_relax_bwd_random_shapes(dev, grid, shape, tau):
+    parity.test_relax_bwd_lion(dev, grid, tau, shape)
