@@ -1,9 +1,10 @@
 """Parity on seeded random shapes: grouped products over random expert counts
 (up to 70, so some batches take two launches) and random token blocks
 (empty ones included), and the relax backward + Lion on random row counts and
-group counts (odd numbers of scale groups included). Each case runs the same
-checks, with the same tolerances, as the fixed-shape tests in
-test_gpu_parity.py."""
+group counts (odd numbers of scale groups included), and the fused second
+product against the separate calls on random expert layouts. Each case runs
+the same checks, with the same tolerances, as the fixed-shape tests in
+test_gpu_parity.py and test_gpu_fused.py."""
 
 import numpy as np
 import pytest
@@ -52,3 +53,37 @@ def test_recon_random_shapes(dev, M, N, K, offs):
                          ids=lambda v: f"{v[0]}x{v[1]}" if isinstance(v, tuple) else str(v))
 def test_relax_bwd_random_shapes(dev, grid, shape, tau):
     parity.test_relax_bwd_lion(dev, grid, tau, shape)
+
+
+def _fused_cases(n, seed=2026):
+    rng = np.random.default_rng(seed)
+    grids = [oracle.GRID_INT2, oracle.GRID_TERNARY, oracle.GRID_INT3_LOCAL, oracle.GRID_INT3]
+    cases = []
+    for i in range(n):
+        E = int(rng.integers(65, 71)) if i == 0 else int(rng.integers(1, 40))
+        counts = [int(c) for c in rng.choice([0, 64, 128, 192], E)]
+        if sum(counts) == 0:
+            counts[0] = 64
+        cases.append((grids[i % 4], int(rng.choice([32, 64, 160, 256])),
+                      int(rng.choice([128, 256, 384])), counts, bool(i % 2 == 0)))
+    return cases
+
+
+@pytest.mark.parametrize("grid,rpe,K,counts,with_next", _fused_cases(6),
+                         ids=lambda v: f"E{len(v)}" if isinstance(v, list) else str(v))
+def test_fused_step_random_layouts(dev, grid, rpe, K, counts, with_next):
+    """The second product fused into backward + Lion (+ next forward) against
+    the separate calls, bit for bit, on random expert layouts."""
+    import torch
+    import post_weight_quantization_philox_amd as g
+    from tests import test_gpu_fused as fused
+    offs, t = fused._state(grid, rpe, K, counts, seed=len(counts) * 7 + rpe, dev=dev)
+    out = fused._both(g, torch, dev, grid, rpe, K, offs, t, with_next)
+    a, b = out["separate"], out["fused"]
+    assert np.isfinite(a["loss"].item())
+    assert torch.equal(a["loss"], b["loss"])
+    assert torch.equal(a["RT"].view(torch.int16), b["RT"].view(torch.int16))
+    for k in ("logits", "mom", "scales", "scale_mom"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a["dW"].view(torch.int16), b["dW"].view(torch.int16))
+    assert not torch.equal(a["logits"], t["logits"])
