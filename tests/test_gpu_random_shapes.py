@@ -1,8 +1,10 @@
 """Parity on seeded random shapes: grouped products over random expert counts
 (up to 70, so some batches take two launches) and random token blocks
 (empty ones included), and the relax backward + Lion on random row counts and
-group counts (odd numbers of scale groups included), and the fused second
-product against the separate calls on random expert layouts. Each case runs
+group counts (odd numbers of scale groups included), the relaxed forward on
+random shapes, the Gram-form product on random layer and token sizes, and
+the fused second product against the separate calls on random expert
+layouts. Each case runs
 the same checks, with the same tolerances, as the fixed-shape tests in
 test_gpu_parity.py and test_gpu_fused.py."""
 
@@ -87,3 +89,27 @@ def test_fused_step_random_layouts(dev, grid, rpe, K, counts, with_next):
         assert torch.equal(a[k], b[k]), k
     assert torch.equal(a["dW"].view(torch.int16), b["dW"].view(torch.int16))
     assert not torch.equal(a["logits"], t["logits"])
+
+
+def _fwd_cases(n, seed=2027):
+    rng = np.random.default_rng(seed)
+    grids = [oracle.GRID_INT2, oracle.GRID_TERNARY, oracle.GRID_INT3_LOCAL, oracle.GRID_INT3]
+    return [(grids[i % 4], float(rng.choice([1.0, 0.3, 0.05])), float(rng.choice([1.0, 0.0])),
+             (int(rng.integers(1, 48)), 128 * int(rng.integers(1, 7)))) for i in range(n)]
+
+
+@pytest.mark.parametrize("grid,tau,eta,shape", _fwd_cases(8),
+                         ids=lambda v: f"{v[0]}x{v[1]}" if isinstance(v, tuple) else str(v))
+def test_relax_fwd_random_shapes(dev, grid, tau, eta, shape):
+    parity.test_relax_fwd(dev, grid, tau, eta, shape)
+
+
+def _gram_cases(n, seed=2028):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 600)), 64 * int(rng.integers(1, 9)), 128 * int(rng.integers(1, 9)))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("M,N,K", _gram_cases(4))
+def test_recon_gram_random_shapes(dev, M, N, K):
+    parity.test_recon_gram(dev, M, N, K)
